@@ -1,0 +1,472 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for DSpark's Markov-head draft calibration and for the
+ * Selector-style top-k truncation of the same rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls this file: only the
+ * tests, the smoke check and the bench's CPU-baseline leg use it.  It shares no code, header,
+ * table or constant with the GPU library; the two meet only through the seeded inputs (made by the
+ * separate input generator) and through the published definition of the noise hash below, which
+ * each side implements on its own.
+ *
+ * Every number is computed in IEEE double precision, one plain loop at a time, in the order the
+ * defining formula states (sums over the rank index j ascending, vocabulary scans v ascending).
+ * Inputs are read exactly: bf16 and fp32 values convert to double without rounding.
+ *
+ * Sources (pages; cited by title and section):
+ *  [MvS]  "DFlash-2's Selector and DSpark's Markov Head: An Equivalence Observation"
+ *         (jialefu.github.io) -- sections "What the two methods do", "The equivalence: remove the
+ *         gate, recover the Markov Head", "Where the parallelism comes from", "Two implications".
+ *  [DSp]  "DSpark" overview (himanshu-arora.com) -- sections "Semi-autoregressive generation",
+ *         "The Markov head", "Confidence-scheduled verification", "Hardware-aware prefix scheduling".
+ *  [Tut]  "DSpark: Repair the Joint, Meter the Verify" (stable-lab.github.io) -- sections
+ *         "Fix 1: A First-Order Markov Head", "Why the normalization has to be local",
+ *         "The Trap: A Product of Marginals", "Marginalization, From Scratch".
+ *  [vLLM] "DSpark" (docs.vllm.ai speculators user guide) -- "Markov Head", "Key Parameters".
+ *
+ * Readings where the pages leave a step open (each listed with its reason in the design notes):
+ *  - position 1 is conditioned on the anchor token;
+ *  - ties in every argmax / top-k go to the lower vocabulary id (never the candidate slot);
+ *  - sampling is Gumbel-max at temperature T: key = l/T + G(seed,b,k,v); greedy ignores T;
+ *  - the reported log-probability is log softmax(l/T)[token] over the same set the pick ranges over;
+ *  - the gate multiplies the predecessor embedding: x = W1[a] (.) H(h_k).
+ *
+ * Parity status: every exported function is pinned by a CPU test against a value the pages print, a
+ * closed form, a special case or brute force; see the test files.  No function here is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_W2_RV 0 /* W2 stored [r, V] as on the pages */
+#define OR_W2_VR 1 /* W2 stored transposed, [V, r] */
+#define OR_GREEDY 0
+#define OR_SAMPLE 1
+
+/* ------------------------------------------------------------------------------------------ */
+/* exact reads of the stored inputs                                                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Element i of a weight tensor stored as fp32 or as raw bf16 bits; both widen exactly. */
+static double weight_at(const void* p, int dtype, size_t i) {
+    if (dtype == OR_F32) return (double)((const float*)p)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* W2[j, v] in either storage order ([MvS] "What the two methods do": W2 is 256 x V). */
+static double w2_at(const void* W2, int dtype, int layout, int V, int r, int j, int v) {
+    size_t i = (layout == OR_W2_RV) ? (size_t)j * (size_t)V + (size_t)v : (size_t)v * (size_t)r + (size_t)j;
+    return weight_at(W2, dtype, i);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* noise: counter-based hash of (seed, row, position, vocabulary id)                            */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Finalisation mix of MurmurHash3 (A. Appleby, public domain): xor-shift 16, multiply by
+ * 0x85EBCA6B, xor-shift 13, multiply by 0xC2B2AE35, xor-shift 16, all modulo 2^32. */
+static uint32_t murmur3_fmix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    h *= 0xC2B2AE35u;
+    h ^= h >> 16;
+    return h;
+}
+
+uint32_t oracle_fmix32(uint32_t h) { return murmur3_fmix32(h); }
+
+/* Chained key: k0 from the 64-bit seed, then the row, the position and the vocabulary id are
+ * folded in one at a time, each followed by a full finalisation mix. */
+uint32_t oracle_noise_bits(uint64_t seed, uint32_t row, uint32_t pos, uint32_t v) {
+    uint32_t k0 = murmur3_fmix32((uint32_t)(seed & 0xFFFFFFFFu) ^ murmur3_fmix32((uint32_t)(seed >> 32)));
+    uint32_t k1 = murmur3_fmix32(k0 ^ row);
+    uint32_t k2 = murmur3_fmix32(k1 ^ pos);
+    return murmur3_fmix32(k2 ^ v);
+}
+
+/* Uniform in (0,1): the top 23 bits m of the hash give u = (2m + 1) / 2^24, never 0 or 1. */
+double oracle_noise_uniform(uint64_t seed, uint32_t row, uint32_t pos, uint32_t v) {
+    uint32_t h = oracle_noise_bits(seed, row, pos, v);
+    return (2.0 * (double)(h >> 9) + 1.0) / 16777216.0;
+}
+
+/* Standard Gumbel variate G = -ln(-ln u) (inverse CDF of exp(-exp(-g))). */
+double oracle_gumbel(uint64_t seed, uint32_t row, uint32_t pos, uint32_t v) {
+    double u = oracle_noise_uniform(seed, row, pos, v);
+    return -log(-log(u));
+}
+
+/* Noise of n consecutive vocabulary ids v0 .. v0+n-1 at one (row, position): uniforms and Gumbel
+ * variates (either output may be NULL).  Same definitions as above, one call per id. */
+void oracle_noise_fill(uint64_t seed, uint32_t row, uint32_t pos, uint32_t v0, int64_t n, double* u, double* g) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        if (u) u[i] = oracle_noise_uniform(seed, row, pos, v0 + (uint32_t)i);
+        if (g) g[i] = oracle_gumbel(seed, row, pos, v0 + (uint32_t)i);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* gate  H = sigmoid(h Wg)                                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [MvS] "What the two methods do": the Selector's gate H(h_t) is computed from the current hidden
+ * state; [vLLM] "Markov Head": the gated variant gates the bias by the backbone hidden state.  The
+ * form is a sigmoid of a linear map with no bias: H[i, j] = 1 / (1 + exp(-sum_d h[i,d] Wg[d,j])).
+ * h is [rows, D] bf16, Wg is [D, r] bf16, H is [rows, r]. */
+void oracle_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, double* H) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < rows; ++i) {
+        for (int j = 0; j < r; ++j) {
+            double z = 0.0;
+            for (int d = 0; d < D; ++d)
+                z += weight_at(h, OR_BF16, (size_t)i * D + d) * weight_at(Wg, OR_BF16, (size_t)d * r + j);
+            H[(size_t)i * r + j] = 1.0 / (1.0 + exp(-z));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* one calibrated position                                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Predecessor embedding x[j] = W1[prev, j] * H[j] (H == NULL means the ungated head, H = 1).
+ * [MvS] "The equivalence": gated form logits_t = U_t + (W1[a] (.) H(h_t))^T W2. */
+static void predecessor_embedding(const void* W1, int dtype, int r, int prev, const double* Hk, double* x) {
+    for (int j = 0; j < r; ++j) {
+        double w = weight_at(W1, dtype, (size_t)prev * r + j);
+        x[j] = Hk ? w * Hk[j] : w;
+    }
+}
+
+/* Calibrated logit of candidate v: U_k(v) + sum_j x[j] W2[j, v]  ([MvS] "The equivalence",
+ * per-candidate form; [DSp] "The Markov head": one matrix-vector product over the vocabulary). */
+static double calibrated_logit(const float* Uk, const void* W2, int dtype, int layout, int V, int r,
+                               const double* x, int v) {
+    double bias = 0.0;
+    for (int j = 0; j < r; ++j) bias += x[j] * w2_at(W2, dtype, layout, V, r, j, v);
+    return (double)Uk[v] + bias;
+}
+
+/* Pick over a set of n logits l[0..n) whose vocabulary ids are ids[0..n) (ids == NULL: id = slot).
+ * key = l (greedy) or l/T + G(seed,row,pos,id) (Gumbel-max, [DSp] "DSpark vs DFlash 2": sample from
+ * the corrected logits).  Ties go to the lower vocabulary id.  Returns the slot picked; writes the
+ * top-2 key margin and the log-softmax of l/T at the pick ([Tut] "Why the normalization has to be
+ * local": the exact per-position probability of the drawn token). */
+static int pick(const double* l, const int32_t* ids, int n, int mode, uint64_t seed, int row, int pos,
+                double T, double* margin, double* logprob, double* lse_out) {
+    int best = -1;
+    double k1 = -INFINITY, k2 = -INFINITY;
+    for (int s = 0; s < n; ++s) {
+        int id = ids ? ids[s] : s;
+        double key = (mode == OR_SAMPLE) ? l[s] / T + oracle_gumbel(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)id) : l[s];
+        int better = (best < 0) || key > k1 || (key == k1 && id < (ids ? ids[best] : best));
+        if (better) {
+            if (best >= 0) k2 = k1;
+            k1 = key;
+            best = s;
+        } else if (key > k2) {
+            k2 = key;
+        }
+    }
+    double Teff = (mode == OR_SAMPLE) ? T : 1.0;
+    double M = -INFINITY;
+    for (int s = 0; s < n; ++s)
+        if (l[s] / Teff > M) M = l[s] / Teff;
+    double sum = 0.0;
+    for (int s = 0; s < n; ++s) sum += exp(l[s] / Teff - M);
+    double lse = M + log(sum);
+    if (margin) *margin = k1 - k2;
+    if (logprob) *logprob = l[best] / Teff - lse;
+    if (lse_out) *lse_out = lse;
+    return best;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O-M: full-vocabulary Markov head, K serial positions                                         */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [DSp] "Semi-autoregressive generation" / "The Markov head", [Tut] "Fix 1": for k = 0..K-1 the bias
+ * W1[prev]^T W2 is added to U_k and a token is picked over the full vocabulary; the token becomes the
+ * predecessor of position k+1.  Position 0's predecessor is the anchor.
+ *
+ * U: [B, K, V] fp32.  W1: [V, r].  W2: [r, V] or [V, r] (layout).  anchor: [B].
+ * H: [B, K, r] gate values or NULL.  follow: [B, K] or NULL -- when given, the predecessor of position
+ * k > 0 is follow[b, k-1] instead of the oracle's own pick (teacher forcing along a given path).
+ * rows: list of nrows row ids to compute (NULL: all B rows).
+ * Outputs at [b*K + k]: tokens, logprobs (log softmax at the pick), margins (top-2 key gap),
+ * lp_follow (log softmax at follow[b,k], or NULL), best_logit (l at the pick, or NULL). */
+void oracle_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                         const int32_t* anchor, const double* H, int B, int K, int V, int r, int mode,
+                         uint64_t seed, double temperature, const int32_t* follow, const int32_t* rows,
+                         int nrows, int32_t* tokens, double* logprobs, double* margins, double* lp_follow,
+                         double* best_logit) {
+    int n = rows ? nrows : B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n; ++ri) {
+        int b = rows ? rows[ri] : ri;
+        double* l = (double*)malloc(sizeof(double) * (size_t)V);
+        double* x = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        int prev = anchor[b];
+        for (int k = 0; k < K; ++k) {
+            const float* Uk = U + ((size_t)b * K + k) * (size_t)V;
+            const double* Hk = H ? H + ((size_t)b * K + k) * (size_t)r : NULL;
+            predecessor_embedding(W1, wdtype, r, prev, Hk, x);
+            for (int v = 0; v < V; ++v) l[v] = calibrated_logit(Uk, W2, wdtype, w2_layout, V, r, x, v);
+            double margin, lp, lse;
+            int tok = pick(l, NULL, V, mode, seed, b, k, temperature, &margin, &lp, &lse);
+            size_t o = (size_t)b * K + k;
+            tokens[o] = tok;
+            if (logprobs) logprobs[o] = lp;
+            if (margins) margins[o] = margin;
+            if (best_logit) best_logit[o] = l[tok];
+            double Teff = (mode == OR_SAMPLE) ? temperature : 1.0;
+            if (follow) {
+                if (lp_follow) lp_follow[o] = l[follow[o]] / Teff - lse;
+                prev = follow[o];
+            } else {
+                prev = tok;
+            }
+        }
+        free(l);
+        free(x);
+    }
+}
+
+/* Calibrated logits of one position for every row, given each row's predecessor:
+ * out[b, v] = U_k[b, v] + sum_j x_b[j] W2[j, v] with x_b = W1[prev[b]] (.) H_k[b].
+ * Uk rows are u_stride floats apart; H_k is [B, r] or NULL.  rows/nrows select rows (NULL: all);
+ * out is indexed [b*V + v]. */
+void oracle_markov_logits(const float* Uk, int64_t u_stride, const void* W1, const void* W2, int wdtype,
+                          int w2_layout, const int32_t* prev, const double* Hk, int B, int V, int r,
+                          const int32_t* rows, int nrows, double* out) {
+    int n = rows ? nrows : B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n; ++ri) {
+        int b = rows ? rows[ri] : ri;
+        double* x = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        predecessor_embedding(W1, wdtype, r, prev[b], Hk ? Hk + (size_t)b * r : NULL, x);
+        for (int v = 0; v < V; ++v)
+            out[(size_t)b * V + v] = calibrated_logit(Uk + (size_t)b * u_stride, W2, wdtype, w2_layout, V, r, x, v);
+        free(x);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O-T: top-k candidates of the base logits                                                     */
+/* ------------------------------------------------------------------------------------------ */
+
+/* "a before b" in the candidate order: larger value first, equal values (including -0 == +0) by the
+ * lower vocabulary id. */
+static int ranks_before(float va, int ia, float vb, int ib) {
+    if (va > vb) return 1;
+    if (va < vb) return 0;
+    return ia < ib;
+}
+
+/* First k ids of one row of base logits u[0..V) in the order (value desc, id asc).  One ascending
+ * scan keeps the first k of that order seen so far (insertion into a sorted list of length k), which
+ * yields exactly the first k of the full sort. */
+static void topk_row(const float* u, int V, int k, int32_t* id, float* vv) {
+    int have = 0;
+    for (int v = 0; v < V; ++v) {
+        float x = u[v];
+        if (have == k && !ranks_before(x, v, vv[k - 1], id[k - 1])) continue;
+        int pos = (have < k) ? have : k - 1;
+        while (pos > 0 && ranks_before(x, v, vv[pos - 1], id[pos - 1])) {
+            vv[pos] = vv[pos - 1];
+            id[pos] = id[pos - 1];
+            --pos;
+        }
+        vv[pos] = x;
+        id[pos] = v;
+        if (have < k) ++have;
+    }
+}
+
+/* [MvS] "Where the parallelism comes from": at each position keep the top-k tokens under the base
+ * logits.  Definition: sort all V ids by (U desc, id asc) and keep the first k.
+ * U: [rows, V] with rows u_stride floats apart.  idx: [rows, k]; val: [rows, k] or NULL.
+ * Requires 1 <= k <= V. */
+void oracle_topk(const float* U, int64_t u_stride, int rows, int V, int k, int32_t* idx, float* val) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int row = 0; row < rows; ++row) {
+        float* vv = (float*)malloc(sizeof(float) * (size_t)k);
+        topk_row(U + (size_t)row * u_stride, V, k, idx + (size_t)row * k, vv);
+        if (val)
+            for (int s = 0; s < k; ++s) val[(size_t)row * k + s] = vv[s];
+        free(vv);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O-R: the Markov head restricted to given candidate sets                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+/* The plain definition of what the truncated execution computes: O-M with the vocabulary at position
+ * k replaced by the candidate set cand[b, k, 0..topk).  Pick, margin and log-softmax range over that
+ * set.  Same argument meaning as oracle_markov_draft; cand is [B, K, topk]. */
+void oracle_markov_restricted(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                              const int32_t* anchor, const double* H, const int32_t* cand, int B, int K,
+                              int V, int r, int topk, int mode, uint64_t seed, double temperature,
+                              const int32_t* rows, int nrows, int32_t* tokens, double* logprobs,
+                              double* margins) {
+    int n = rows ? nrows : B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n; ++ri) {
+        int b = rows ? rows[ri] : ri;
+        double* l = (double*)malloc(sizeof(double) * (size_t)topk);
+        double* x = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        int prev = anchor[b];
+        for (int k = 0; k < K; ++k) {
+            const float* Uk = U + ((size_t)b * K + k) * (size_t)V;
+            const double* Hk = H ? H + ((size_t)b * K + k) * (size_t)r : NULL;
+            const int32_t* c = cand + ((size_t)b * K + k) * (size_t)topk;
+            predecessor_embedding(W1, wdtype, r, prev, Hk, x);
+            for (int s = 0; s < topk; ++s) l[s] = calibrated_logit(Uk, W2, wdtype, w2_layout, V, r, x, c[s]);
+            double margin, lp;
+            int slot = pick(l, c, topk, mode, seed, b, k, temperature, &margin, &lp, NULL);
+            size_t o = (size_t)b * K + k;
+            tokens[o] = c[slot];
+            if (logprobs) logprobs[o] = lp;
+            if (margins) margins[o] = margin;
+            prev = c[slot];
+        }
+        free(l);
+        free(x);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O-S: the Selector, step by step                                                              */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [MvS] "Where the parallelism comes from", in its order:
+ *  1. fix the candidate sets: top-k of U at every position (O-T);
+ *  2. precompute every calibration inside those sets: the anchor row
+ *       T0[j]      = U_0(c_0j)  + < A[anchor] (.) H_0, Bemb[c_0j] >
+ *     and for t = 1..K-1 the k x k table of predecessor i, candidate j
+ *       T_t[i][j]  = U_t(c_tj) + < A[c_{t-1,i}] (.) H_t, Bemb[c_tj] >
+ *     ([MvS] "What the two methods do": S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>);
+ *  3. walk: pick over the anchor row, then over row i_{t-1} of each table (greedy, or Gumbel-max with
+ *     the noise keyed on the vocabulary id of the candidate).
+ * A, Bemb: [V, r].  H: [B, K, r] or NULL.  cand_out: [B, K, topk] or NULL.
+ * tables_out: [B, topk + (K-1)*topk*topk] (anchor row, then the tables) or NULL.
+ * logprobs: log softmax of the walked row's scores/T at the pick. */
+void oracle_selector_draft(const float* U, const void* A, const void* Bemb, int wdtype, const int32_t* anchor,
+                           const double* H, int B, int K, int V, int r, int topk, int mode, uint64_t seed,
+                           double temperature, const int32_t* rows, int nrows, int32_t* tokens,
+                           double* logprobs, double* margins, int32_t* cand_out, double* tables_out) {
+    int n = rows ? nrows : B;
+    size_t tstride = (size_t)topk + (size_t)(K > 0 ? K - 1 : 0) * topk * topk;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n; ++ri) {
+        int b = rows ? rows[ri] : ri;
+        int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)K * topk);
+        double* tab = (double*)malloc(sizeof(double) * tstride);
+        double* row = (double*)malloc(sizeof(double) * (size_t)topk);
+        /* 1. candidate sets */
+        float* cval = (float*)malloc(sizeof(float) * (size_t)topk);
+        for (int t = 0; t < K; ++t)
+            topk_row(U + ((size_t)b * K + t) * (size_t)V, V, topk, cand + (size_t)t * topk, cval);
+        free(cval);
+        /* 2. all pair scores */
+        for (int t = 0; t < K; ++t) {
+            const float* Ut = U + ((size_t)b * K + t) * (size_t)V;
+            const double* Ht = H ? H + ((size_t)b * K + t) * (size_t)r : NULL;
+            int npred = (t == 0) ? 1 : topk;
+            for (int i = 0; i < npred; ++i) {
+                int a = (t == 0) ? anchor[b] : cand[(size_t)(t - 1) * topk + i];
+                for (int j = 0; j < topk; ++j) {
+                    int c = cand[(size_t)t * topk + j];
+                    double dot = 0.0;
+                    for (int q = 0; q < r; ++q) {
+                        double ag = weight_at(A, wdtype, (size_t)a * r + q);
+                        if (Ht) ag = ag * Ht[q];
+                        dot += ag * weight_at(Bemb, wdtype, (size_t)c * r + q);
+                    }
+                    size_t o = (t == 0) ? (size_t)j : (size_t)topk + ((size_t)(t - 1) * topk + i) * topk + j;
+                    tab[o] = (double)Ut[c] + dot;
+                }
+            }
+        }
+        /* 3. the walk */
+        int islot = 0;
+        for (int t = 0; t < K; ++t) {
+            const double* src = (t == 0) ? tab : tab + topk + ((size_t)(t - 1) * topk + islot) * topk;
+            for (int j = 0; j < topk; ++j) row[j] = src[j];
+            double margin, lp;
+            islot = pick(row, cand + (size_t)t * topk, topk, mode, seed, b, t, temperature, &margin, &lp, NULL);
+            size_t o = (size_t)b * K + t;
+            tokens[o] = cand[(size_t)t * topk + islot];
+            if (logprobs) logprobs[o] = lp;
+            if (margins) margins[o] = margin;
+        }
+        if (cand_out) memcpy(cand_out + (size_t)b * K * topk, cand, sizeof(int32_t) * (size_t)K * topk);
+        if (tables_out) memcpy(tables_out + (size_t)b * tstride, tab, sizeof(double) * tstride);
+        free(cand);
+        free(tab);
+        free(row);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* O-B: brute-force enumeration of every path of one row                                        */
+/* ------------------------------------------------------------------------------------------ */
+
+/* log q(path) = sum_k [ l_k(t_k | t_{k-1}) / T - LSE_k(t_{k-1}) ] with t_{-1} = anchor, for all V^K
+ * paths (path index = sum_k t_k V^(K-1-k)).  [Tut] "Fix 1": the draft distribution is the product of
+ * K locally normalised first-order factors.  U: [K, V] (one row), H: [K, r] or NULL.
+ * Returns -1 (and computes nothing) unless V <= 64 and V^K <= 2^20. */
+int oracle_enumerate_paths(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                           int32_t anchor, const double* H, int K, int V, int r, double temperature,
+                           double* logq) {
+    if (V <= 0 || V > 64 || K <= 0 || K > 32) return -1;
+    double count = pow((double)V, (double)K);
+    if (count > 1048576.0) return -1;
+    long np = (long)count;
+    /* log_cond[k][a][v] = log softmax over v of l_k(v | a)/T, for every predecessor a
+     * (position 0 only needs a = anchor). */
+    double* lc = (double*)malloc(sizeof(double) * (size_t)K * V * V);
+    double* l = (double*)malloc(sizeof(double) * (size_t)V);
+    double* x = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+    for (int k = 0; k < K; ++k) {
+        for (int a = 0; a < V; ++a) {
+            int pred = (k == 0) ? anchor : a;
+            predecessor_embedding(W1, wdtype, r, pred, H ? H + (size_t)k * r : NULL, x);
+            double M = -INFINITY;
+            for (int v = 0; v < V; ++v) {
+                l[v] = calibrated_logit(U + (size_t)k * V, W2, wdtype, w2_layout, V, r, x, v) / temperature;
+                if (l[v] > M) M = l[v];
+            }
+            double sum = 0.0;
+            for (int v = 0; v < V; ++v) sum += exp(l[v] - M);
+            double lse = M + log(sum);
+            for (int v = 0; v < V; ++v) lc[((size_t)k * V + a) * V + v] = l[v] - lse;
+        }
+    }
+    for (long p = 0; p < np; ++p) {
+        long rem = p;
+        int path[32];
+        for (int k = K - 1; k >= 0; --k) {
+            path[k] = (int)(rem % V);
+            rem /= V;
+        }
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int a = (k == 0) ? 0 : path[k - 1]; /* row index into lc; position 0 was built from the anchor */
+            s += lc[((size_t)k * V + a) * V + path[k]];
+        }
+        logq[p] = s;
+    }
+    free(lc);
+    free(l);
+    free(x);
+    return 0;
+}

@@ -1,0 +1,425 @@
+"""Pins of the fp64 CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each test names what it pins: a value the pages print, a closed form, a special case that reduces to
+a textbook/library routine, an invariant, or brute force on tiny inputs.  Nothing here compares the
+oracle with itself.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle as O
+import synth as S
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def f64(w):
+    """Stored weights (float32, or uint16 bf16 bits) as exact float64."""
+    return S.bf16_to_f32(w).astype(np.float64) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
+def rng_weights(rng, shape, sigma, dtype):
+    w = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    return S.f32_to_bf16(w) if dtype == "bf16" else w
+
+
+# ------------------------------------------------------------------------------------------ noise
+
+def test_fmix32_published_vectors():
+    """MurmurHash3's finaliser against the published empty-key verification vectors."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "murmur3_fmix32.txt")) if l.strip() and l[0] != "#"]
+    assert len(rows) == 3
+    for seed, expect in rows:
+        assert O.fmix32(int(seed, 16)) == int(expect, 16)
+
+
+def test_noise_uniform_is_odd_lattice_in_open_interval():
+    u, _ = O.noise_fill(0x5EED, 3, 5, 0, 1 << 16)
+    assert np.all(u > 0) and np.all(u < 1)
+    m = u * 2.0 ** 24
+    assert np.all(m == np.round(m)) and np.all(np.round(m).astype(np.int64) % 2 == 1)
+
+
+def test_noise_uniform_chi2():
+    u, _ = O.noise_fill(0x1234, 7, 2, 0, 1 << 20)
+    counts = np.bincount((u * 256).astype(np.int64), minlength=256)
+    chi2 = ((counts - u.size / 256) ** 2 / (u.size / 256)).sum()
+    assert stats.chi2.sf(chi2, 255) > 1e-4
+
+
+def test_gumbel_moments_and_transform():
+    """Closed form: a standard Gumbel has mean = Euler-Mascheroni and variance pi^2/6."""
+    gs, us = [], []
+    for pos in range(4):
+        u, g = O.noise_fill(0x5EED, 11, pos, 0, 1 << 20)
+        gs.append(g)
+        us.append(u)
+    g = np.concatenate(gs)
+    u = np.concatenate(us)
+    n = g.size
+    sigma2 = math.pi ** 2 / 6
+    assert abs(g.mean() - np.euler_gamma) < 5 * math.sqrt(sigma2 / n)
+    # var of the sample variance: (mu4 - sigma^4)/n with mu4 = (3 + 12/5) sigma^4
+    assert abs(g.var() - sigma2) < 5 * sigma2 * math.sqrt(4.4 / n)
+    # G = -log(-log(u)) as numpy computes it
+    np.testing.assert_allclose(g[:4096], -np.log(-np.log(u[:4096])), rtol=0, atol=1e-15)
+    # support of the 23-bit lattice
+    assert g.min() > -2.82 and g.max() < 16.65
+
+
+def test_noise_depends_on_every_key_field():
+    base = O.noise_bits(0x5EED, 1, 2, 3)
+    assert O.noise_bits(0x5EED + 1, 1, 2, 3) != base
+    assert O.noise_bits(0x5EED, 0, 2, 3) != base
+    assert O.noise_bits(0x5EED, 1, 3, 3) != base
+    assert O.noise_bits(0x5EED, 1, 2, 4) != base
+    assert O.noise_bits(0x5EED | (1 << 40), 1, 2, 3) != base
+
+
+# ------------------------------------------------------------------------------------ the bias term
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", [O.W2_RV, O.W2_VR])
+def test_logits_match_numpy_matmul(dtype, layout):
+    """Library routine: U_k + W1[prev] @ W2 by numpy float64 matmul, in both storage orders."""
+    rng = np.random.default_rng(1)
+    B, V, r = 5, 37, 12
+    U = rng.standard_normal((B, V)).astype(np.float32)
+    W1 = rng_weights(rng, (V, r), 0.7, dtype)
+    W2 = rng_weights(rng, (r, V), 0.7, dtype)
+    prev = rng.integers(0, V, B).astype(np.int32)
+    W2s = W2 if layout == O.W2_RV else np.ascontiguousarray(W2.T)
+    got = O.markov_logits(U, W1, W2s, prev, w2_layout=layout)
+    want = U.astype(np.float64) + f64(W1)[prev] @ f64(W2)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    assert np.abs(want - U).max() > 0.5  # the bias is not negligible here
+
+
+def test_logits_onehot_closed_form():
+    """Closed form: W1[a] = e_(a mod r) makes the bias row a copy of W2[a mod r, :], exactly."""
+    rng = np.random.default_rng(2)
+    B, V, r = 6, 50, 8
+    U = rng.standard_normal((B, V)).astype(np.float32)
+    W1 = np.zeros((V, r), np.float32)
+    W1[np.arange(V), np.arange(V) % r] = 1.0
+    W2 = rng.standard_normal((r, V)).astype(np.float32)
+    prev = np.array([0, 3, 7, 8, 13, 49], np.int32)
+    got = O.markov_logits(U, W1, W2, prev)
+    want = U.astype(np.float64) + W2[prev % r].astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_logits_rank1_closed_form():
+    """Closed form: W1[a] = alpha_a u and W2[:, v] = beta_v w give bias = alpha_a beta_v (u . w)."""
+    rng = np.random.default_rng(3)
+    B, V, r = 4, 33, 16
+    alpha = rng.integers(-4, 5, V).astype(np.float64) / 4
+    beta = rng.integers(-4, 5, V).astype(np.float64) / 8
+    u = rng.integers(-3, 4, r).astype(np.float64)
+    w = rng.integers(-3, 4, r).astype(np.float64)
+    W1 = np.outer(alpha, u).astype(np.float32)
+    W2 = np.outer(w, beta).astype(np.float32)
+    U = rng.standard_normal((B, V)).astype(np.float32)
+    prev = rng.integers(0, V, B).astype(np.int32)
+    got = O.markov_logits(U, W1, W2, prev)
+    want = U.astype(np.float64) + np.outer(alpha[prev], beta) * float(u @ w)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------- the pick and chain
+
+def test_w2_zero_greedy_is_per_position_argmax():
+    """Special case ("markov rank 0 disables the head"): with W2 = 0 the greedy draft is the
+    per-position argmax of U, ties to the lower id, and the log-probability is log softmax(U)."""
+    rng = np.random.default_rng(4)
+    B, K, V, r = 6, 5, 40, 8
+    U = np.round(rng.standard_normal((B, K, V)) * 2).astype(np.float32)  # many exact ties
+    W1 = rng.standard_normal((V, r)).astype(np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    res = O.markov_draft(U, W1, W2, anchor)
+    U64 = U.astype(np.float64)
+    assert np.array_equal(res["tokens"], np.argmax(U64, axis=-1))
+    want_lp = np.take_along_axis(U64, res["tokens"][..., None].astype(np.int64), -1)[..., 0] - special.logsumexp(U64, -1)
+    np.testing.assert_allclose(res["logprobs"], want_lp, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_w2_zero_sample_is_gumbel_max_of_U(T):
+    rng = np.random.default_rng(5)
+    B, K, V, r = 4, 3, 64, 8
+    U = rng.standard_normal((B, K, V)).astype(np.float32)
+    W1 = rng.standard_normal((V, r)).astype(np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    res = O.markov_draft(U, W1, W2, anchor, mode=O.SAMPLE, seed=99, temperature=T)
+    for b in range(B):
+        for k in range(K):
+            _, g = O.noise_fill(99, b, k, 0, V)
+            key = U[b, k].astype(np.float64) / T + g
+            assert res["tokens"][b, k] == int(np.argmax(key))
+            lp = U[b, k].astype(np.float64) / T - special.logsumexp(U[b, k].astype(np.float64) / T)
+            assert abs(res["logprobs"][b, k] - lp[res["tokens"][b, k]]) < 1e-12
+
+
+def _strong_tiny(V=5, K=3, r=4, seed=6, gated=False):
+    rng = np.random.default_rng(seed)
+    U = (rng.standard_normal((1, K, V)) * 1.5).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.9).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.9).astype(np.float32)
+    anchor = np.array([rng.integers(0, V)], np.int32)
+    H = rng.uniform(0.1, 1.0, (1, K, r)) if gated else None
+    return U, W1, W2, anchor, H
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("T", [1.0, 1.6])
+def test_enumeration_is_normalised(gated, T):
+    """Local normalisation: the K locally normalised factors make a distribution over all V^K paths."""
+    U, W1, W2, anchor, H = _strong_tiny(gated=gated)
+    logq = O.enumerate_paths(U[0], W1, W2, anchor[0], H_row=None if H is None else H[0], temperature=T)
+    assert abs(np.exp(logq).sum() - 1.0) < 1e-12
+
+
+def test_follow_logprob_sums_to_path_probability():
+    """Brute force: sum over positions of the per-position log-probability of a path equals the
+    enumerated log q of that path (the draft distribution is the product of local factors)."""
+    U, W1, W2, anchor, _ = _strong_tiny(V=6, K=3)
+    logq = O.enumerate_paths(U[0], W1, W2, anchor[0])
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        path = rng.integers(0, 6, 3).astype(np.int32)
+        res = O.markov_draft(U, W1, W2, anchor, follow=path[None])
+        assert abs(res["lp_follow"][0].sum() - logq[tuple(path)]) < 1e-12
+
+
+def test_greedy_chain_matches_brute_force_conditionals():
+    """Brute force: the first greedy token maximises the enumerated marginal q(t1) (which equals the
+    local softmax because later factors sum to one); each later token maximises q(prefix, t)."""
+    for seed in range(8):
+        U, W1, W2, anchor, _ = _strong_tiny(V=5, K=3, seed=100 + seed)
+        q = np.exp(O.enumerate_paths(U[0], W1, W2, anchor[0]))
+        res = O.markov_draft(U, W1, W2, anchor)
+        t = res["tokens"][0]
+        assert t[0] == np.argmax(q.sum(axis=(1, 2)))
+        assert t[1] == np.argmax(q[t[0]].sum(axis=1))
+        assert t[2] == np.argmax(q[t[0], t[1]])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_gumbel_max_sampler_matches_enumerated_distribution(gated):
+    """Statistics against brute force: one row replicated over 2^16 rows (the noise keys on the row)
+    gives independent samples whose path frequencies follow the enumerated q (chi-square)."""
+    V, K, r = 4, 2, 4
+    U, W1, W2, anchor, H = _strong_tiny(V=V, K=K, r=r, seed=8, gated=gated)
+    q = np.exp(O.enumerate_paths(U[0], W1, W2, anchor[0], H_row=None if H is None else H[0]))
+    n = 1 << 16
+    Ub = np.repeat(U, n, axis=0)
+    Hb = None if H is None else np.repeat(H, n, axis=0)
+    res = O.markov_draft(Ub, W1, W2, np.repeat(anchor, n), H=Hb, mode=O.SAMPLE, seed=0xABCD)
+    idx = res["tokens"][:, 0] * V + res["tokens"][:, 1]
+    counts = np.bincount(idx, minlength=V ** K)
+    expect = q.reshape(-1) * n
+    keep = expect > 5
+    chi2 = ((counts[keep] - expect[keep]) ** 2 / expect[keep]).sum()
+    assert stats.chi2.sf(chi2, keep.sum() - 1) > 1e-4
+    # the reported log-probability of every sample is its exact local log-softmax: sum = log q(path)
+    lq = np.log(q.reshape(-1))[idx[:100]]
+    np.testing.assert_allclose(res["logprobs"][:100].sum(axis=1), lq, rtol=0, atol=1e-12)
+
+
+def _np_torch(L=40.0, markov=True):
+    """The page's np/torch example: ids 0 = anchor 'x =', 1 = np, 2 = torch, 3 = .array, 4 = .tensor."""
+    V, K, r = 5, 2, 2
+    U = np.full((1, K, V), -L, np.float32)
+    U[0, 0, [1, 2]] = 0.0
+    U[0, 1, [3, 4]] = 0.0
+    W1 = np.zeros((V, r), np.float32)
+    W1[1] = (1, 0)
+    W1[2] = (0, 1)
+    W2 = np.zeros((r, V), np.float32)
+    if markov:
+        W2[:, 3] = (0, -L)
+        W2[:, 4] = (-L, 0)
+    return U, W1, W2, np.zeros(1, np.int32)
+
+
+def _golden_tables():
+    t = {}
+    for line in open(os.path.join(GOLDEN, "np_torch_tables.txt")):
+        if line.strip() and line[0] != "#":
+            k, *vals = line.split()
+            t[k] = vals
+    return (np.array(t["joint"], float).reshape(2, 2), np.array(t["product"], float).reshape(2, 2),
+            math.log(2) if t["kl_joint_product"] == ["ln2"] else None)
+
+
+def test_np_torch_worked_example_tables():
+    """Values the page prints: the Markov head reproduces the joint table; with the head disabled the
+    draft is the product of the marginals; KL(joint || product) = total correlation = ln 2."""
+    joint, product, kl = _golden_tables()
+    q = np.exp(O.enumerate_paths(*[a[0] if i in (0, 3) else a for i, a in enumerate(_np_torch())]))
+    np.testing.assert_allclose(q[1:3, 3:5], joint, rtol=0, atol=1e-12)
+    assert abs(q.sum() - 1) < 1e-12
+    U, W1, W2, anchor = _np_torch(markov=False)
+    q0 = np.exp(O.enumerate_paths(U[0], W1, W2, anchor[0]))
+    np.testing.assert_allclose(q0[1:3, 3:5], product, rtol=0, atol=1e-12)
+    p = q[1:3, 3:5]
+    prod = np.outer(p.sum(1), p.sum(0))
+    nz = p > 1e-300
+    assert abs((p[nz] * np.log(p[nz] / prod[nz])).sum() - kl) < 1e-9
+
+
+def test_np_torch_sampled_pairs_never_splice():
+    """The page's sampled table: with the Markov head the off-diagonal cells (np .tensor, torch
+    .array) receive no samples, the diagonal about half each; without it each cell gets a quarter."""
+    n = 1 << 14
+    for markov, want in ((True, np.array([[0.5, 0], [0, 0.5]])), (False, np.full((2, 2), 0.25))):
+        U, W1, W2, anchor = _np_torch(markov=markov)
+        res = O.markov_draft(np.repeat(U, n, 0), W1, W2, np.repeat(anchor, n), mode=O.SAMPLE, seed=0x5EED)
+        t = res["tokens"]
+        tab = np.zeros((2, 2))
+        np.add.at(tab, (t[:, 0] - 1, t[:, 1] - 3), 1)
+        assert tab.sum() == n
+        if markov:
+            assert tab[0, 1] == 0 and tab[1, 0] == 0
+        frac = tab / n
+        assert np.all(np.abs(frac - want) < 5 * np.sqrt(np.maximum(want * (1 - want), 1e-12) / n) + 1e-12)
+
+
+# --------------------------------------------------------------------------------------------- gate
+
+def test_gate_matches_numpy_and_zero_weights():
+    rng = np.random.default_rng(9)
+    rows, D, r = 7, 64, 16
+    h = S.f32_to_bf16(rng.standard_normal((rows, D)).astype(np.float32))
+    Wg = S.f32_to_bf16((rng.standard_normal((D, r)) * 0.2).astype(np.float32))
+    H = O.gate(h, Wg)
+    want = 1.0 / (1.0 + np.exp(-(f64(h) @ f64(Wg))))
+    np.testing.assert_allclose(H, want, rtol=0, atol=1e-14)
+    H0 = O.gate(h, np.zeros_like(Wg))
+    assert np.all(H0 == 0.5)  # sigma(0) = 1/2 exactly
+
+
+def test_gate_ones_is_ungated_and_half_halves_bias():
+    """[MvS] "The equivalence": H = 1 recovers the ungated head exactly; H = 1/2 halves the bias."""
+    rng = np.random.default_rng(10)
+    B, K, V, r = 3, 4, 30, 8
+    U = rng.standard_normal((B, K, V)).astype(np.float32)
+    W1 = rng.standard_normal((V, r)).astype(np.float32)
+    W2 = rng.standard_normal((r, V)).astype(np.float32)
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    a = O.markov_draft(U, W1, W2, anchor, mode=O.SAMPLE, seed=3)
+    b = O.markov_draft(U, W1, W2, anchor, H=np.ones((B, K, r)), mode=O.SAMPLE, seed=3)
+    for key in ("tokens", "logprobs", "margins"):
+        assert np.array_equal(a[key], b[key])
+    prev = rng.integers(0, V, B).astype(np.int32)
+    l1 = O.markov_logits(U[:, 0], W1, W2, prev)
+    lh = O.markov_logits(U[:, 0], W1, W2, prev, Hk=np.full((B, r), 0.5))
+    np.testing.assert_allclose(lh - U[:, 0], 0.5 * (l1 - U[:, 0]), rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("k", [1, 16, 61])
+def test_topk_matches_lexsort(k):
+    """Textbook routine: a full sort by (value desc, id asc); ties and signed zeros included."""
+    rng = np.random.default_rng(11)
+    rows, V = 40, 61
+    U = np.round(rng.standard_normal((rows, V)) * 2).astype(np.float32)
+    U[0] = 0.0
+    U[1, ::2] = -0.0
+    U[2, :] = 5.0
+    U[3, ::3] = np.float32(3.0)
+    idx, val = O.topk(U, k)
+    for i in range(rows):
+        order = np.lexsort((np.arange(V), -U[i].astype(np.float64)))[:k]
+        assert np.array_equal(idx[i], order)
+        assert np.array_equal(val[i], U[i, order])
+
+
+# ----------------------------------------------------------------------------------------- selector
+
+@pytest.mark.parametrize("mode", [O.GREEDY, O.SAMPLE])
+@pytest.mark.parametrize("gated", [False, True])
+def test_selector_equals_markov_restricted_to_its_candidates(mode, gated):
+    """[MvS] "Two implications": the Selector is the (gated) Markov head executed on fixed top-k sets;
+    with W1 := A and W2 := Bemb^T it must equal the head restricted to the same candidate sets."""
+    rng = np.random.default_rng(12)
+    B, K, V, r, topk = 4, 5, 48, 8, 6
+    U = (rng.standard_normal((B, K, V)) * 2).astype(np.float32)
+    A = S.f32_to_bf16((rng.standard_normal((V, r)) * 0.8).astype(np.float32))
+    Bemb = S.f32_to_bf16((rng.standard_normal((V, r)) * 0.8).astype(np.float32))
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    H = rng.uniform(0, 1, (B, K, r)) if gated else None
+    sel = O.selector_draft(U, A, Bemb, anchor, H=H, topk=topk, mode=mode, seed=21, temperature=0.9)
+    cand, _ = O.topk(U, topk)
+    assert np.array_equal(sel["cand"], cand)
+    res = O.markov_restricted(U, A, Bemb, anchor, cand, w2_layout=O.W2_VR, H=H, mode=mode, seed=21, temperature=0.9)
+    for key in ("tokens", "logprobs", "margins"):
+        assert np.array_equal(sel[key], res[key])
+    assert np.all(np.isin(sel["tokens"], cand.reshape(B, -1)))
+
+
+@pytest.mark.parametrize("mode", [O.GREEDY, O.SAMPLE])
+def test_selector_with_topk_V_is_the_full_head(mode):
+    """Special case: with the candidate set equal to the whole vocabulary the truncation is exact,
+    in sampling too because the noise keys on the vocabulary id, not the candidate slot."""
+    w = S.workload("tiny", V=64)
+    sel = O.selector_draft(w.U, w.W1, np.ascontiguousarray(w.W2.T), w.anchor, topk=w.V, mode=mode, seed=5)
+    full = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=5)
+    assert np.array_equal(sel["tokens"], full["tokens"])
+    np.testing.assert_allclose(sel["logprobs"], full["logprobs"], rtol=0, atol=1e-12)
+
+
+def test_selector_tables_match_numpy():
+    rng = np.random.default_rng(13)
+    B, K, V, r, topk = 2, 4, 30, 8, 5
+    U = rng.standard_normal((B, K, V)).astype(np.float32)
+    A = rng.standard_normal((V, r)).astype(np.float32)
+    Bemb = rng.standard_normal((V, r)).astype(np.float32)
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    H = rng.uniform(0, 1, (B, K, r))
+    sel = O.selector_draft(U, A, Bemb, anchor, H=H, topk=topk)
+    A64, B64 = A.astype(np.float64), Bemb.astype(np.float64)
+    for b in range(B):
+        c = sel["cand"][b]
+        T0 = U[b, 0, c[0]] + (A64[anchor[b]] * H[b, 0]) @ B64[c[0]].T
+        np.testing.assert_allclose(sel["tables"][b, :topk], T0, rtol=0, atol=1e-12)
+        for t in range(1, K):
+            Tt = U[b, t, c[t]][None, :] + (A64[c[t - 1]] * H[b, t][None, :]) @ B64[c[t]].T
+            got = sel["tables"][b, topk + (t - 1) * topk * topk: topk + t * topk * topk].reshape(topk, topk)
+            np.testing.assert_allclose(got, Tt, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------- invariants
+
+def test_rows_are_independent_and_restricted_full_sets_is_full():
+    w = S.strong("tiny", B=4, V=96, K=3)
+    full = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=7)
+    one = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=7, rows=[2])
+    assert np.array_equal(one["tokens"][2], full["tokens"][2])
+    assert np.all(one["tokens"][[0, 1, 3]] == -1)
+    cand = np.broadcast_to(np.arange(w.V, dtype=np.int32), (w.B, w.K, w.V))
+    res = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand, mode=O.SAMPLE, seed=7)
+    assert np.array_equal(res["tokens"], full["tokens"])
+    np.testing.assert_allclose(res["logprobs"], full["logprobs"], rtol=0, atol=1e-12)
+
+
+def test_shift_invariance():
+    """Adding a constant to every base logit of a position changes neither the pick nor the
+    log-probability (softmax and Gumbel-max are shift invariant).  The shifted U is re-rounded to
+    fp32 (spacing 2^-13 near 1024), so picks are compared where the margin exceeds that rounding."""
+    w = S.strong("tiny", B=3, V=80, K=4)
+    U2 = (w.U.astype(np.float64) + 1024.0).astype(np.float32)
+    for mode in (O.GREEDY, O.SAMPLE):
+        a = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=1)
+        b = O.markov_draft(U2, w.W1, w.W2, w.anchor, mode=mode, seed=1)
+        ok = a["margins"] > 1e-3
+        assert ok.mean() > 0.9
+        assert np.array_equal(a["tokens"][ok], b["tokens"][ok])
+        np.testing.assert_allclose(a["logprobs"], b["logprobs"], rtol=0, atol=1e-3)
