@@ -1,0 +1,201 @@
+/*
+ * dspark.h -- C ABI of libdspark: DSpark's semi-autoregressive draft calibration on one AMD MI355X
+ * (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *  - The Markov head.  "DFlash-2's Selector and DSpark's Markov Head: An Equivalence Observation",
+ *    section "What the two methods do": logits_k = U_k + W1[a]^T W2 with W1 in R^{V x r},
+ *    W2 in R^{r x V} and a the previously sampled token; the DSpark overview, section "The Markov
+ *    head": W1 is an embedding lookup and W2 projects back to the vocabulary, one matrix-vector
+ *    product per position, positions taken left to right ("Semi-autoregressive generation").
+ *  - The gated variant.  Same page, section "The equivalence: remove the gate, recover the Markov
+ *    Head": logits_t = U_t + (W1[a] (.) H(h_t))^T W2.
+ *  - The Selector execution.  Same page, section "Where the parallelism comes from": keep the top-k
+ *    tokens of the base logits at every position, compute the calibrated scores of all k x k
+ *    adjacent (predecessor, candidate) pairs in parallel, then walk.
+ *  - The drawn token's exact local log-probability.  "DSpark: Repair the Joint, Meter the Verify",
+ *    section "Why the normalization has to be local": a softmax over the vocabulary of one position.
+ *
+ * Conventions for every call below:
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous memory owned by the caller.  The
+ *    library never allocates or frees memory inside these calls; scratch memory is the caller's
+ *    `workspace`, sized by the matching *_workspace_bytes call.
+ *  - Every call enqueues work on `stream` (a hipStream_t passed as void*, NULL = the null stream)
+ *    and returns after enqueueing, without synchronising with the device.
+ *  - Host-detectable argument errors return before anything is enqueued and leave every output
+ *    untouched: DSPARK_EINVAL (NULL required pointer, size <= 0, unknown enum, temperature <= 0 in
+ *    sampling mode, top-k out of range), DSPARK_EWORKSPACE (workspace too small or NULL when
+ *    needed), DSPARK_EUNSUPPORTED (a shape outside the documented limits).  A failed kernel launch
+ *    returns DSPARK_EDEVICE.  dspark_last_error() gives a one-line reason for the calling thread's
+ *    last non-OK status.  No C++ exception crosses this boundary.
+ *  - Preconditions not checked on the host: token ids (anchor, prev) lie in [0, V); U, H and the
+ *    weights are finite.  Violations give unspecified results.
+ *  - Token ties: every argmax, Gumbel-max, top-k and walk breaks ties towards the lower vocabulary id.
+ *  - Determinism: identical inputs, seed and shapes give bit-identical outputs on one device.
+ *  - Calls on one stream run in order; concurrent calls need distinct workspaces.
+ *
+ * Noise (sampling mode).  The pages fix no generator.  Gumbel noise G(seed, b, k, v) is derived from a
+ * counter hash: fmix(x) is the MurmurHash3 32-bit finalisation mix (A. Appleby, public domain);
+ * k0 = fmix(lo32(seed) ^ fmix(hi32(seed))), k1 = fmix(k0 ^ b), k2 = fmix(k1 ^ k), h = fmix(k2 ^ v);
+ * u = (2 * (h >> 9) + 1) / 2^24; G = -ln(-ln u).  b is the batch row, k the draft position (0-based),
+ * v the vocabulary id (never a candidate slot).  The pick is argmax_v of l_v / T + G(seed, b, k, v).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+
+/* status codes */
+#define DSPARK_OK 0
+#define DSPARK_EINVAL 1
+#define DSPARK_EUNSUPPORTED 2
+#define DSPARK_EWORKSPACE 3
+#define DSPARK_EDEVICE 4
+
+/* weight element types (U, H and all outputs are always fp32 / int32) */
+#define DSPARK_F32 0
+#define DSPARK_BF16 1 /* raw bfloat16, 2 bytes per element */
+
+/* storage order of W2 */
+#define DSPARK_W2_RV 0 /* [r, V]: as the pages write W2 */
+#define DSPARK_W2_VR 1 /* [V, r]: W2 transposed, one r-vector per vocabulary id (same layout as Bemb) */
+
+/* pick rule */
+#define DSPARK_GREEDY 0 /* argmax of the calibrated logits; temperature ignored (T = 1) */
+#define DSPARK_SAMPLE 1 /* Gumbel-max at temperature T: an exact sample of softmax(l / T) */
+
+/* Version of this ABI (DSPARK_ABI_VERSION of the built library). */
+int dspark_abi_version(void);
+
+/* Static string naming a status code. */
+const char* dspark_status_str(int status);
+
+/* One-line reason for the calling thread's most recent non-OK status ("" if none). */
+const char* dspark_last_error(void);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Markov head                                                                                      */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* Workspace bytes dspark_markov_draft / dspark_markov_step need for these sizes (0 on bad sizes). */
+size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int w2_layout);
+
+/*
+ * Draft K positions for B rows with the Markov head (the DSpark overview, sections "Semi-autoregressive
+ * generation" and "The Markov head"; the equivalence page, section "What the two methods do").
+ * For k = 0 .. K-1 and every row b, with a_0 = anchor[b] and a_k = tokens[b, k-1]:
+ *     l[v]          = U[b, k, v] + sum_j x[j] * W2[j, v],   x = W1[a_k, :] (.) H[b, k, :]  (H == NULL: x = W1[a_k])
+ *     tokens[b, k]  = argmax_v key(v),   key = l[v] (GREEDY) or l[v] / T + G(seed, b, k, v) (SAMPLE)
+ *     logprobs[b,k] = l[tok] / T - log sum_v exp(l[v] / T)   (T = 1 in GREEDY)
+ *
+ * U        [B, K, V] fp32.
+ * W1       [V, r] weights of type wdtype.
+ * W2       [r, V] (w2_layout = DSPARK_W2_RV) or [V, r] (DSPARK_W2_VR) of type wdtype.  The bf16 matrix-core
+ *          path reads the [V, r] layout; an [r, V] W2 is first transposed into the workspace on every call,
+ *          so callers that draft repeatedly should transpose once with dspark_pack_w2.
+ * anchor   [B] int32, the token each row's block starts from.
+ * H        [B, K, r] fp32 gate values (for example from dspark_gate) or NULL for the ungated head.
+ * r        1 .. 1024.  The bf16 matrix-core path needs r % 16 == 0 and r <= 512; other shapes run on a
+ *          vector-ALU path of the same results.
+ * mode     DSPARK_GREEDY or DSPARK_SAMPLE; seed and temperature (> 0) are used in SAMPLE mode only.
+ * tokens   [B, K] int32 output.   logprobs: [B, K] fp32 output or NULL.
+ * Accumulation is fp32 over bf16 (or fp32) products; the gated bf16 path rounds x to bf16 (nearest even).
+ */
+int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                        const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                        uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * One position of the same rule with the predecessors supplied by the caller (teacher forcing).
+ * U_k      [B, V] fp32 with row b at U_k + b * u_stride (u_stride >= V).
+ * prev     [B] int32 predecessors.   H_k: [B, r] fp32 or NULL.   k: the draft position, used only as the
+ *          noise counter in SAMPLE mode.
+ * tok      [B] int32 output.  logprob, best_logit: [B] fp32 outputs or NULL (best_logit = l[tok]).
+ */
+int dspark_markov_step(const float* U_k, int64_t u_stride, const void* W1, const void* W2, int wdtype,
+                       int w2_layout, const int32_t* prev, const float* H_k, int B, int V, int r, int k, int mode,
+                       uint64_t seed, float temperature, int32_t* tok, float* logprob, float* best_logit,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Validation call: the calibrated logits of one position, written out as out[b, v] = l[v] (fp32,
+ * [B, V]), computed with the same bias contraction the drafting kernels use.  Arguments as
+ * dspark_markov_step.  Needs no workspace for the [V, r] layout; with an [r, V] W2 it needs
+ * V * r * (2 or 4) bytes of workspace for the transposed copy.
+ */
+int dspark_markov_logits(const float* U_k, int64_t u_stride, const void* W1, const void* W2, int wdtype,
+                         int w2_layout, const int32_t* prev, const float* H_k, int B, int V, int r, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Transpose W2 from [r, V] to [V, r] (element type wdtype): dst[v, j] = src[j, v].  Both device
+ * buffers hold V * r elements and must not overlap.
+ */
+int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, void* stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* gate                                                                                             */
+/* ------------------------------------------------------------------------------------------------ */
+
+/*
+ * H = sigmoid(h Wg): the context gate of the gated head and of the Selector (equivalence page,
+ * section "What the two methods do": H(h_t) is computed from the current hidden state; the speculators
+ * guide, "Markov Head": the gated variant gates the bias by the backbone hidden state).  The pages give
+ * no formula; this library takes a bias-free linear map followed by the logistic sigmoid.
+ * h [rows, D] bf16, Wg [D, r] bf16, H [rows, r] fp32 output.  fp32 accumulation.
+ * D % 32 == 0 and r % 32 == 0 are required (DSPARK_EUNSUPPORTED otherwise).
+ */
+int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Selector-style top-k truncation                                                                  */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* Workspace bytes dspark_topk needs (0 on bad sizes). */
+size_t dspark_topk_workspace_bytes(int rows, int V, int topk);
+
+/*
+ * Top-k of every row of U under the order (value desc, vocabulary id asc); -0.0 and +0.0 compare
+ * equal.  (Equivalence page, section "Where the parallelism comes from": the candidate set of a
+ * position is the top tokens under the base logits.)
+ * U [rows, V] fp32 with row i at U + i * u_stride.  idx [rows, topk] int32 output, val [rows, topk]
+ * fp32 output or NULL.  1 <= topk <= min(V, 64).
+ */
+int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dspark_selector_draft needs (0 on bad sizes). */
+size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk);
+
+/*
+ * Selector execution of the (optionally gated) Markov rule (equivalence page, sections "Where the
+ * parallelism comes from" and "Two implications"):
+ *  1. cand[b, t, :] = top-k of U[b, t, :];
+ *  2. pair scores, all in parallel: the anchor row  S0[b, j] = U[b,0,c_0j] + < A[anchor_b] (.) H[b,0], Bemb[c_0j] >
+ *     and for t >= 1  S_t[b, i, j] = U[b,t,c_tj] + < A[c_{t-1,i}] (.) H[b,t], Bemb[c_tj] >;
+ *  3. the walk: i_0 = pick over S0[b, :], i_t = pick over S_t[b, i_{t-1}, :]; tokens[b, t] = c_{t, i_t}.
+ *     The pick is the same GREEDY / SAMPLE rule as the Markov head over the k candidates, keyed on
+ *     vocabulary ids; logprobs[b, t] = log softmax over the walked row of scores / T.
+ * U [B, K, V] fp32; A, Bemb [V, r] of type wdtype; anchor [B]; H [B, K, r] fp32 or NULL.
+ * topk 1 .. min(V, 64); r % 8 == 0 and r <= 1024 for bf16 (r % 4 == 0 for fp32).
+ * tokens [B, K] int32 output; logprobs [B, K] fp32 or NULL; cand [B, K, topk] int32 or NULL;
+ * scores [B, topk + (K-1) * topk * topk] fp32 or NULL (anchor row, then the K-1 tables, row-major i, j).
+ */
+int dspark_selector_draft(const float* U, const void* A, const void* Bemb, int wdtype, const int32_t* anchor,
+                          const float* H, int B, int K, int V, int r, int topk, int mode, uint64_t seed,
+                          float temperature, int32_t* tokens, float* logprobs, int32_t* cand, float* scores,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,373 @@
+// api.hip -- the extern "C" boundary of libdspark: argument checks, workspace carving, dispatch.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dspark.h"
+#include "internal.hpp"
+
+namespace dspark {
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int device_fail(hipError_t e, const char* what) {
+    return fail(DSPARK_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxG = 1024;          // upper bound on workgroups along the vocabulary
+constexpr int kRowPad = 128;         // partials are padded to whole 128-row blocks
+constexpr int kMfmaWGPerCU = 2;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+struct MarkovWs {
+    Partials part;
+    int Bpad;
+    void* w2t;  // transposed W2 (only when an [r, V] bf16 W2 is drafted on the matrix-core path)
+};
+
+bool mfma_eligible(int wdtype, int r) { return wdtype == DSPARK_BF16 && mfma_supported_r(r); }
+
+size_t markov_ws_bytes(int B, int V, int r, int wdtype, int w2_layout, bool need_pack) {
+    const size_t Bpad = (size_t)round_up(B, kRowPad);
+    size_t bytes = 5 * align256(sizeof(float) * kMaxG * Bpad);
+    if (need_pack && w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) bytes += align256((size_t)V * r * 2);
+    return bytes;
+}
+
+MarkovWs carve_markov(void* ws, int B) {
+    MarkovWs w{};
+    w.Bpad = round_up(B, kRowPad);
+    uint8_t* p = (uint8_t*)ws;
+    const size_t one = align256(sizeof(float) * kMaxG * (size_t)w.Bpad);
+    w.part.key = (float*)p;
+    w.part.idx = (int*)(p + one);
+    w.part.l = (float*)(p + 2 * one);
+    w.part.m = (float*)(p + 3 * one);
+    w.part.s = (float*)(p + 4 * one);
+    w.w2t = p + 5 * one;
+    return w;
+}
+
+int check_common(const void* W1, const void* W2, int wdtype, int w2_layout, int B, int V, int r, int mode,
+                 float temperature) {
+    if (!W1 || !W2) return fail(DSPARK_EINVAL, "W1 and W2 must not be NULL");
+    if (B <= 0 || V <= 0 || r <= 0) return fail(DSPARK_EINVAL, "B, V and r must be positive (B=%d V=%d r=%d)", B, V, r);
+    if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(DSPARK_EINVAL, "unknown weight dtype %d", wdtype);
+    if (w2_layout != DSPARK_W2_RV && w2_layout != DSPARK_W2_VR) return fail(DSPARK_EINVAL, "unknown W2 layout %d", w2_layout);
+    if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE) return fail(DSPARK_EINVAL, "unknown mode %d", mode);
+    if (mode == DSPARK_SAMPLE && !(temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0 when sampling");
+    if (r > 1024) return fail(DSPARK_EUNSUPPORTED, "r = %d exceeds 1024", r);
+    if (B > 65535 * 4) return fail(DSPARK_EUNSUPPORTED, "B = %d too large", B);
+    return DSPARK_OK;
+}
+
+// One position: contraction + calibration + pick (or logits store), then the cross-workgroup reduction.
+int run_step(const float* Uk, int64_t u_stride, const void* W1, const void* W2, int wdtype, int w2_layout,
+             const int32_t* prev, int64_t prev_stride, const float* Hk, int64_t h_stride, int B, int V, int r, int k,
+             int mode, uint32_t k0, float temperature, int32_t* tok, float* lp, float* bestl, int64_t out_stride,
+             const MarkovWs* ws, float* logits_out, hipStream_t st) {
+    const bool store = logits_out != nullptr;
+    const int kmode = store ? kModeStore : (mode == DSPARK_SAMPLE ? kModeSample : kModeGreedy);
+    const float teff = (mode == DSPARK_SAMPLE) ? temperature : 1.0f;
+    const float c = kLog2e / teff;
+    const bool gated = Hk != nullptr;
+    const int ncu = device_cu_count();
+    const bool use_mfma = mfma_eligible(wdtype, r) && w2_layout == DSPARK_W2_VR && aligned16(W1) && aligned16(W2) &&
+                          (!gated || (aligned16(Hk) && h_stride % 4 == 0));
+    Partials part{};
+    int Bpad = 0;
+    if (!store) {
+        part = ws->part;
+        Bpad = ws->Bpad;
+    }
+    int G = 0;
+    hipError_t e;
+    if (use_mfma) {
+        StepArgs a{};
+        a.U = Uk;
+        a.u_stride = u_stride;
+        a.W1 = (const uint16_t*)W1;
+        a.W2t = (const uint16_t*)W2;
+        a.prev = prev;
+        a.prev_stride = prev_stride;
+        a.H = Hk;
+        a.h_stride = h_stride;
+        a.B = B;
+        a.V = V;
+        a.r = r;
+        a.k = k;
+        a.k0 = k0;
+        a.c = c;
+        a.ntiles = (V + 31) / 32;
+        a.part = part;
+        a.Bpad = Bpad;
+        a.logits_out = logits_out;
+        G = a.ntiles < ncu * kMfmaWGPerCU ? a.ntiles : ncu * kMfmaWGPerCU;
+        if (G > kMaxG) G = kMaxG;
+        const bool vec_u = (V % 4 == 0) && (u_stride % 4 == 0) && aligned16(Uk);
+        e = launch_markov_step_mfma(a, kmode, gated, vec_u, G, st);
+    } else {
+        StepArgsValu a{};
+        a.U = Uk;
+        a.u_stride = u_stride;
+        a.W1 = W1;
+        a.W2 = W2;
+        a.sj = (w2_layout == DSPARK_W2_RV) ? V : 1;
+        a.sv = (w2_layout == DSPARK_W2_RV) ? 1 : r;
+        a.prev = prev;
+        a.prev_stride = prev_stride;
+        a.H = Hk;
+        a.h_stride = h_stride;
+        a.B = B;
+        a.V = V;
+        a.r = r;
+        a.k = k;
+        a.k0 = k0;
+        a.c = c;
+        a.part = part;
+        a.Bpad = Bpad;
+        a.logits_out = logits_out;
+        const int nblk = (V + 255) / 256;
+        G = nblk < ncu * 4 ? nblk : ncu * 4;
+        if (G > kMaxG) G = kMaxG;
+        e = launch_markov_step_valu(a, wdtype == DSPARK_BF16, kmode, gated, G, st);
+    }
+    if (e != hipSuccess) return device_fail(e, "markov step launch");
+    if (store) return DSPARK_OK;
+    ReduceArgs ra{};
+    ra.part = part;
+    ra.G = G;
+    ra.Bpad = Bpad;
+    ra.inv_t = 1.0f / teff;
+    ra.tokens = tok;
+    ra.logprobs = lp;
+    ra.best_logit = bestl;
+    ra.out_stride = out_stride;
+    e = launch_markov_reduce(ra, B, st);
+    if (e != hipSuccess) return device_fail(e, "markov reduce launch");
+    return DSPARK_OK;
+}
+
+}  // namespace
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+int dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_status_str(int status) {
+    switch (status) {
+        case DSPARK_OK: return "DSPARK_OK";
+        case DSPARK_EINVAL: return "DSPARK_EINVAL";
+        case DSPARK_EUNSUPPORTED: return "DSPARK_EUNSUPPORTED";
+        case DSPARK_EWORKSPACE: return "DSPARK_EWORKSPACE";
+        case DSPARK_EDEVICE: return "DSPARK_EDEVICE";
+        default: return "DSPARK_UNKNOWN_STATUS";
+    }
+}
+
+const char* dspark_last_error(void) { return g_err; }
+
+size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int w2_layout) {
+    if (B <= 0 || K <= 0 || V <= 0 || r <= 0) return 0;
+    return markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
+}
+
+int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, void* stream) {
+    g_err[0] = 0;
+    if (!src_rv || !dst_vr) return fail(DSPARK_EINVAL, "NULL buffer");
+    if (V <= 0 || r <= 0) return fail(DSPARK_EINVAL, "V and r must be positive");
+    if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(DSPARK_EINVAL, "unknown weight dtype %d", wdtype);
+    hipError_t e = launch_transpose(src_rv, r, V, wdtype == DSPARK_BF16 ? 2 : 4, dst_vr, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "transpose launch");
+    return DSPARK_OK;
+}
+
+int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                        const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode, uint64_t seed,
+                        float temperature, int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    g_err[0] = 0;
+    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
+    if (rc) return rc;
+    if (!U || !anchor || !tokens) return fail(DSPARK_EINVAL, "U, anchor and tokens must not be NULL");
+    if (K <= 0) return fail(DSPARK_EINVAL, "K must be positive");
+    const size_t need = markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    MarkovWs ws = carve_markov(workspace, B);
+    const void* W2use = W2;
+    int layout = w2_layout;
+    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {
+        hipError_t e = launch_transpose(W2, r, V, 2, ws.w2t, st);
+        if (e != hipSuccess) return device_fail(e, "transpose launch");
+        W2use = ws.w2t;
+        layout = DSPARK_W2_VR;
+    }
+    const uint32_t k0 = noise_key0(seed);
+    for (int k = 0; k < K; ++k) {
+        const int32_t* prev = (k == 0) ? anchor : tokens + (k - 1);
+        const int64_t pstride = (k == 0) ? 1 : K;
+        rc = run_step(U + (size_t)k * V, (int64_t)K * V, W1, W2use, wdtype, layout, prev, pstride,
+                      H ? H + (size_t)k * r : nullptr, (int64_t)K * r, B, V, r, k, mode, k0, temperature, tokens + k,
+                      logprobs ? logprobs + k : nullptr, nullptr, K, &ws, nullptr, st);
+        if (rc) return rc;
+    }
+    return DSPARK_OK;
+}
+
+int dspark_markov_step(const float* U_k, int64_t u_stride, const void* W1, const void* W2, int wdtype, int w2_layout,
+                       const int32_t* prev, const float* H_k, int B, int V, int r, int k, int mode, uint64_t seed,
+                       float temperature, int32_t* tok, float* logprob, float* best_logit, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
+    if (rc) return rc;
+    if (!U_k || !prev || !tok) return fail(DSPARK_EINVAL, "U_k, prev and tok must not be NULL");
+    if (u_stride < V) return fail(DSPARK_EINVAL, "u_stride %lld < V %d", (long long)u_stride, V);
+    if (k < 0) return fail(DSPARK_EINVAL, "k must be >= 0");
+    const size_t need = markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    MarkovWs ws = carve_markov(workspace, B);
+    const void* W2use = W2;
+    int layout = w2_layout;
+    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {
+        hipError_t e = launch_transpose(W2, r, V, 2, ws.w2t, st);
+        if (e != hipSuccess) return device_fail(e, "transpose launch");
+        W2use = ws.w2t;
+        layout = DSPARK_W2_VR;
+    }
+    return run_step(U_k, u_stride, W1, W2use, wdtype, layout, prev, 1, H_k, r, B, V, r, k, mode, noise_key0(seed),
+                    temperature, tok, logprob, best_logit, 1, &ws, nullptr, st);
+}
+
+int dspark_markov_logits(const float* U_k, int64_t u_stride, const void* W1, const void* W2, int wdtype, int w2_layout,
+                         const int32_t* prev, const float* H_k, int B, int V, int r, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, DSPARK_GREEDY, 1.0f);
+    if (rc) return rc;
+    if (!U_k || !prev || !out) return fail(DSPARK_EINVAL, "U_k, prev and out must not be NULL");
+    if (u_stride < V) return fail(DSPARK_EINVAL, "u_stride %lld < V %d", (long long)u_stride, V);
+    hipStream_t st = (hipStream_t)stream;
+    const void* W2use = W2;
+    int layout = w2_layout;
+    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {
+        const size_t need = (size_t)V * r * 2;
+        if (!workspace || workspace_bytes < need)
+            return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed for the transposed W2", need);
+        hipError_t e = launch_transpose(W2, r, V, 2, workspace, st);
+        if (e != hipSuccess) return device_fail(e, "transpose launch");
+        W2use = workspace;
+        layout = DSPARK_W2_VR;
+    }
+    return run_step(U_k, u_stride, W1, W2use, wdtype, layout, prev, 1, H_k, r, B, V, r, 0, DSPARK_GREEDY, 0, 1.0f,
+                    nullptr, nullptr, nullptr, 1, nullptr, out, st);
+}
+
+int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* stream) {
+    g_err[0] = 0;
+    if (!h || !Wg || !H) return fail(DSPARK_EINVAL, "NULL buffer");
+    if (rows <= 0 || D <= 0 || r <= 0) return fail(DSPARK_EINVAL, "rows, D and r must be positive");
+    if (D % 256 != 0 || r % 32 != 0)
+        return fail(DSPARK_EUNSUPPORTED, "gate needs D %% 256 == 0 and r %% 32 == 0 (D=%d r=%d)", D, r);
+    if (!aligned16(h) || !aligned16(Wg)) return fail(DSPARK_EINVAL, "h and Wg must be 16-byte aligned");
+    if (rows > 65535 * 32) return fail(DSPARK_EUNSUPPORTED, "too many rows");
+    hipError_t e = launch_gate((const uint16_t*)h, (const uint16_t*)Wg, rows, D, r, H, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "gate launch");
+    return DSPARK_OK;
+}
+
+size_t dspark_topk_workspace_bytes(int rows, int V, int topk) {
+    if (rows <= 0 || V <= 0 || topk <= 0) return 0;
+    return 256;  // no scratch is used; a non-zero size keeps the calling convention uniform
+}
+
+int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!U || !idx) return fail(DSPARK_EINVAL, "U and idx must not be NULL");
+    if (rows <= 0 || V <= 0) return fail(DSPARK_EINVAL, "rows and V must be positive");
+    if (u_stride < V) return fail(DSPARK_EINVAL, "u_stride < V");
+    if (topk < 1 || topk > V) return fail(DSPARK_EINVAL, "topk %d outside [1, V]", topk);
+    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 16 needs V <= 4096");
+    hipError_t e = launch_topk(U, u_stride, rows, V, topk, idx, val, nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "topk launch");
+    return DSPARK_OK;
+}
+
+size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk) {
+    if (B <= 0 || K <= 0 || V <= 0 || r <= 0 || topk <= 0) return 0;
+    const size_t tstride = (size_t)topk + (size_t)(K - 1) * topk * topk;
+    return align256(sizeof(int32_t) * (size_t)B * K * topk) + align256(sizeof(float) * (size_t)B * tstride);
+}
+
+int dspark_selector_draft(const float* U, const void* A, const void* Bemb, int wdtype, const int32_t* anchor,
+                          const float* H, int B, int K, int V, int r, int topk, int mode, uint64_t seed,
+                          float temperature, int32_t* tokens, float* logprobs, int32_t* cand, float* scores,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!U || !A || !Bemb || !anchor || !tokens) return fail(DSPARK_EINVAL, "U, A, Bemb, anchor, tokens must not be NULL");
+    if (B <= 0 || K <= 0 || V <= 0 || r <= 0) return fail(DSPARK_EINVAL, "B, K, V and r must be positive");
+    if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(DSPARK_EINVAL, "unknown weight dtype %d", wdtype);
+    if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE) return fail(DSPARK_EINVAL, "unknown mode %d", mode);
+    if (mode == DSPARK_SAMPLE && !(temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0 when sampling");
+    if (topk < 1 || topk > V) return fail(DSPARK_EINVAL, "topk %d outside [1, V]", topk);
+    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 16 needs V <= 4096");
+    if (r > 1024) return fail(DSPARK_EUNSUPPORTED, "r = %d exceeds 1024", r);
+    if ((size_t)B * K > 2147483647u) return fail(DSPARK_EUNSUPPORTED, "B * K too large");
+    const size_t need = dspark_selector_workspace_bytes(B, K, V, r, topk);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* p = (uint8_t*)workspace;
+    int32_t* cand_ws = (int32_t*)p;
+    float* scores_ws = (float*)(p + align256(sizeof(int32_t) * (size_t)B * K * topk));
+    SelectorArgs a{};
+    a.U = U;
+    a.A = A;
+    a.Bemb = Bemb;
+    a.bf16 = wdtype == DSPARK_BF16;
+    a.anchor = anchor;
+    a.H = H;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.r = r;
+    a.topk = topk;
+    a.sample = mode == DSPARK_SAMPLE;
+    a.k0 = noise_key0(seed);
+    a.inv_t = a.sample ? 1.0f / temperature : 1.0f;
+    a.cand = cand ? cand : cand_ws;
+    a.scores = scores ? scores : scores_ws;
+    a.tokens = tokens;
+    a.logprobs = logprobs;
+    hipError_t e = launch_topk(U, V, B * K, V, topk, const_cast<int32_t*>(a.cand), nullptr, nullptr, st);
+    if (e != hipSuccess) return device_fail(e, "topk launch");
+    e = launch_pair_scores(a, st);
+    if (e != hipSuccess) return device_fail(e, "pair-score launch");
+    e = launch_walk(a, st);
+    if (e != hipSuccess) return device_fail(e, "walk launch");
+    return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// gate.hip -- H = sigmoid(h Wg) for every draft position at once.
+//
+// The equivalence page ("DFlash-2's Selector and DSpark's Markov Head"), section "What the two methods
+// do", computes the gate H(h_t) from the current hidden state; the pages give no formula, and this
+// library takes a bias-free linear map followed by the logistic sigmoid.  The product is one bf16
+// matrix-core GEMM [rows, D] x [D, r] with fp32 accumulation, off the serial draft loop.
+//
+// Workgroup = four waves sharing one 32 x 32 output tile; wave w accumulates the k-range
+// [w D/4, (w+1) D/4) (split-K inside the workgroup, summed in a fixed order through LDS, so the result
+// is deterministic).  Per 64-wide k step a wave reads its A fragments (h rows, k-contiguous) straight
+// from global memory and stages the Wg block [64 k x 32 n] transposed through LDS so that B fragments
+// are k-contiguous too.  The next step's loads are issued before the current step's MFMAs.
+#include "internal.hpp"
+
+namespace dspark {
+
+namespace {
+
+constexpr int kGateThreads = 256;
+constexpr int kKStep = 64;                   // k per iteration and wave
+constexpr int kBtStride = kKStep + 8;        // bf16 elements per LDS row of the transposed Wg block
+
+struct GateLoads {
+    u32x4_t a[4];  // h[row][k0 + 16*kk + 8*half .. +8], kk = 0..3
+    u32x4_t w[4];  // Wg[k0 + krow][n0 + 8*nch .. +8] for chunk c = lane + 64*q
+};
+
+__device__ __forceinline__ void gate_load(GateLoads& L, const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
+                                          int rows, int D, int r, int row, int n0, int k0, int lane) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        L.a[kk] = (row < rows) ? *reinterpret_cast<const u32x4_t*>(h + (size_t)row * D + k0 + 16 * kk + 8 * half)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = lane + 64 * q;  // 256 chunks: 64 k-rows x 4 chunks of 8 n
+        const int krow = c >> 2, nch = c & 3;
+        L.w[q] = *reinterpret_cast<const u32x4_t*>(Wg + (size_t)(k0 + krow) * r + n0 + 8 * nch);
+    }
+}
+
+__global__ void __launch_bounds__(kGateThreads) gate_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
+                                                          int rows, int D, int r, float* __restrict__ H) {
+    __shared__ __attribute__((aligned(16))) uint16_t bt[4][32 * kBtStride];
+    __shared__ float red[3][32 * 32];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int row0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+    const int row = row0 + (lane & 31);
+    const int kq = D / 4;
+    const int kbeg = wave * kq, kend = kbeg + kq;
+
+    f32x16_t acc = {};
+    GateLoads cur, nxt;
+    gate_load(cur, h, Wg, rows, D, r, row, n0, kbeg, lane);
+    uint16_t* my = bt[wave];
+    for (int k0 = kbeg; k0 < kend; k0 += kKStep) {
+        if (k0 + kKStep < kend) gate_load(nxt, h, Wg, rows, D, r, row, n0, k0 + kKStep, lane);
+        // transpose the Wg block into LDS: my[n][k]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = lane + 64 * q;
+            const int krow = c >> 2, nch = c & 3;
+            const uint32_t wv[4] = {cur.w[q].x, cur.w[q].y, cur.w[q].z, cur.w[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                my[(8 * nch + 2 * e) * kBtStride + krow] = (uint16_t)(wv[e] & 0xFFFFu);
+                my[(8 * nch + 2 * e + 1) * kBtStride + krow] = (uint16_t)(wv[e] >> 16);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes of this wave done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(my + (lane & 31) * kBtStride + 16 * kk + 8 * half);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.a[kk]), bf, acc, 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (k0 + kKStep < kend) cur = nxt;
+    }
+    // split-K sum in a fixed order: wave 0 + wave 1 + wave 2 + wave 3
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[wave - 1][i * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float z = acc[i];
+            z += red[0][i * 64 + lane];
+            z += red[1][i * 64 + lane];
+            z += red[2][i * 64 + lane];
+            const int m = row0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const int n = n0 + (lane & 31);
+            if (m < rows) H[(size_t)m * r + n] = 1.0f / (1.0f + __expf(-z));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, hipStream_t st) {
+    const dim3 grid((rows + 31) / 32, r / 32), block(kGateThreads);
+    hipLaunchKernelGGL(gate_kernel, grid, block, 0, st, h, Wg, rows, D, r, H);
+    return hipGetLastError();
+}
+
+}  // namespace dspark

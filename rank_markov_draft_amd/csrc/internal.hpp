@@ -1,0 +1,99 @@
+// internal.hpp -- kernel argument blocks and launchers shared between the libdspark translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dspark {
+
+constexpr int kModeGreedy = 0;
+constexpr int kModeSample = 1;
+constexpr int kModeStore = 2;  // validation: write the calibrated logits instead of picking
+
+// One position of the Markov head, matrix-core kernel (bf16, W2 stored [V, r]).
+struct StepArgs {
+    const float* U;         // row b at U + b * u_stride
+    int64_t u_stride;
+    const uint16_t* W1;     // [V, r] bf16 bits
+    const uint16_t* W2t;    // [V, r] bf16 bits
+    const int32_t* prev;    // predecessor of row b at prev[b * prev_stride]
+    int64_t prev_stride;
+    const float* H;         // gate row b at H + b * h_stride (gated kernels only)
+    int64_t h_stride;
+    int B, V, r, k;         // k: position (noise counter)
+    uint32_t k0;            // noise key of the seed
+    float c;                // log2(e) / T  (T = 1 in greedy mode)
+    int ntiles;             // ceil(V / 32)
+    Partials part;          // [G][Bpad]
+    int Bpad;
+    float* logits_out;      // store mode: [B, V]
+};
+
+// Same for the vector-ALU kernel; W2 element (j, v) at W2[j * sj + v * sv].
+struct StepArgsValu {
+    const float* U;
+    int64_t u_stride;
+    const void* W1;
+    const void* W2;
+    int64_t sj, sv;
+    const int32_t* prev;
+    int64_t prev_stride;
+    const float* H;
+    int64_t h_stride;
+    int B, V, r, k;
+    uint32_t k0;
+    float c;
+    Partials part;
+    int Bpad;
+    float* logits_out;
+};
+
+struct ReduceArgs {
+    Partials part;
+    int G, Bpad;
+    float inv_t;            // 1 / T in sampling mode, 1 in greedy mode
+    int32_t* tokens;        // row b at tokens[b * out_stride]
+    float* logprobs;        // same indexing, or null
+    float* best_logit;      // same indexing, or null
+    int64_t out_stride;
+};
+
+int mfma_supported_r(int r);
+hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);
+hipError_t launch_markov_step_valu(const StepArgsValu& a, bool bf16, int mode, bool gated, int G, hipStream_t st);
+hipError_t launch_markov_reduce(const ReduceArgs& a, int B, hipStream_t st);
+
+hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes, void* dst, hipStream_t st);
+
+// gate: H = sigmoid(h Wg)
+hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, hipStream_t st);
+
+// selector
+size_t topk_workspace_bytes(int rows, int V, int topk);
+int topk_supported(int V, int topk);
+hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val,
+                       void* ws, hipStream_t st);
+struct SelectorArgs {
+    const float* U;         // [B, K, V]
+    const void* A;          // [V, r]
+    const void* Bemb;       // [V, r]
+    bool bf16;
+    const int32_t* anchor;
+    const float* H;         // [B, K, r] or null
+    int B, K, V, r, topk;
+    bool sample;
+    uint32_t k0;
+    float inv_t;            // 1/T (sample) or 1
+    const int32_t* cand;    // [B, K, topk]
+    float* scores;          // [B, topk + (K-1) topk^2]
+    int32_t* tokens;
+    float* logprobs;
+};
+hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st);
+hipError_t launch_walk(const SelectorArgs& a, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace dspark

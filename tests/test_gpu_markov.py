@@ -1,0 +1,184 @@
+"""GPU parity of the Markov-head path (dspark_markov_logits / _step / _draft) against the fp64 oracle.
+
+Small shapes span several 32-wide vocabulary tiles, ragged vocabulary tails, ragged 128-row batch blocks,
+both W2 storage orders, fp32 and bf16 weights, every rank path, greedy and Gumbel-max picks, weak (the
+measured recipe) and strong (bias of unit size) weights, and the gate.  Full-size cases run the measured
+workloads in the launch configuration the bench times and compare sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth as S
+from helpers import LOGIT_TOL, check_draft, host, t_f32, t_i32, t_w
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def D():
+    import rank_markov_draft_amd as D
+    return D
+
+
+def _w2(w, layout):
+    return w.W2 if layout == O.W2_RV else np.ascontiguousarray(w.W2.T)
+
+
+def _rand_H(B, K, r, seed=0):
+    return np.random.default_rng(seed).uniform(0.0, 1.0, (B, K, r)).astype(np.float32)
+
+
+# (B, K, V, r, wdtype): tile-spanning small shapes; r=24 and r=48 take the vector-ALU path
+SHAPES = [
+    (1, 4, 512, 16, S.F32),
+    (5, 3, 1000, 64, S.BF16),
+    (130, 2, 777, 32, S.BF16),
+    (3, 3, 100, 24, S.BF16),
+    (4, 2, 600, 48, S.BF16),
+    (2, 2, 300, 512, S.BF16),
+    (7, 2, 257, 16, S.F32),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d-%s" % (s[0], s[1], s[2], s[3], "bf16" if s[4] else "f32"))
+@pytest.mark.parametrize("layout", [O.W2_RV, O.W2_VR], ids=["rv", "vr"])
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+def test_logits_parity(D, shape, layout, gated):
+    B, K, V, r, wd = shape
+    w = S.strong("serving", B=B, K=1, V=V, r=r, wdtype=wd)
+    prev = np.random.default_rng(1).integers(0, V, B).astype(np.int32)
+    H = _rand_H(B, 1, r)[:, 0] if gated else None
+    out = D.dspark_markov_logits(t_f32(w.U[:, 0]), t_w(w.W1), t_w(_w2(w, layout)), t_i32(prev), w2_layout=layout,
+                                 H_k=None if H is None else t_f32(H))
+    got = host(out)
+    ref = O.markov_logits(w.U[:, 0], w.W1, _w2(w, layout), prev, w2_layout=layout,
+                          Hk=None if H is None else H.astype(np.float64))
+    err = np.abs(got - ref).max()
+    # fp32 accumulation of exact products; the gated bf16 path also rounds W1[a] (.) H to bf16
+    assert err <= (LOGIT_TOL if gated and wd == S.BF16 else 1e-3), err
+    assert np.abs(ref - w.U[:, 0]).max() > 0.5  # the bias is far from negligible in this variant
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d" % s[:4])
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+@pytest.mark.parametrize("strength", ["weak", "strong"])
+def test_draft_parity(D, shape, mode, strength):
+    B, K, V, r, wd = shape
+    make = S.strong if strength == "strong" else S.workload
+    w = make("serving", B=B, K=K, V=V, r=r, wdtype=wd, mode=mode)
+    T = 0.8 if mode == S.SAMPLE else 1.0
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), w2_layout=D.DSPARK_W2_VR,
+                                    mode=mode, seed=w.noise_seed, temperature=T)
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=w.noise_seed, temperature=T, follow=tok)
+    check_draft(tok, lp, ref, what=f"{shape} {mode} {strength}")
+
+
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+def test_draft_gated_and_rv_layout(D, mode):
+    w = S.strong("gated", B=9, K=4, V=900, r=64, D=0, mode=mode)
+    H = _rand_H(w.B, w.K, w.r, seed=3)
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2), t_i32(w.anchor), w2_layout=D.DSPARK_W2_RV,
+                                    H=t_f32(H), mode=mode, seed=11)
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, H=H.astype(np.float64), mode=mode, seed=11, follow=tok)
+    check_draft(tok, lp, ref)
+
+
+def test_gate_ones_equals_ungated_bitwise(D):
+    w = S.strong("serving", B=6, K=3, V=700, r=64, mode=S.SAMPLE)
+    a = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), mode=D.DSPARK_SAMPLE, seed=5)
+    b = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), mode=D.DSPARK_SAMPLE, seed=5,
+                              H=t_f32(np.ones((w.B, w.K, w.r), np.float32)))
+    assert np.array_equal(host(a[0]), host(b[0]))
+    assert np.array_equal(host(a[1]), host(b[1]))
+
+
+def test_w2_zero_is_argmax_of_U(D):
+    """The head disabled (W2 = 0): greedy tokens are exactly the per-position argmax of U (ties low)."""
+    w = S.workload("serving", B=3, K=4, V=2000, r=32, mode=S.GREEDY)
+    U = np.round(w.U).astype(np.float32)  # plenty of exact ties
+    W2T = np.zeros_like(w.W2T)
+    tok, lp = D.dspark_markov_draft(t_f32(U), t_w(w.W1), t_w(W2T), t_i32(w.anchor))
+    assert np.array_equal(host(tok), np.argmax(U, axis=-1))
+
+
+def test_step_teacher_forced_and_determinism(D):
+    w = S.strong("serving", B=33, K=3, V=1500, r=128, mode=S.SAMPLE)
+    U = t_f32(w.U)
+    W1, W2 = t_w(w.W1), t_w(w.W2T)
+    rng = np.random.default_rng(4)
+    for k in range(w.K):
+        prev = rng.integers(0, w.V, w.B).astype(np.int32)
+        tok, lp, bl = D.dspark_markov_step(U[:, k], W1, W2, t_i32(prev), k, mode=D.DSPARK_SAMPLE, seed=9)
+        tok2, lp2, _ = D.dspark_markov_step(U[:, k], W1, W2, t_i32(prev), k, mode=D.DSPARK_SAMPLE, seed=9)
+        tok, lp, bl = host(tok), host(lp), host(bl)
+        assert np.array_equal(tok, host(tok2)) and np.array_equal(lp, host(lp2))
+        # oracle at position k with the same predecessors (the noise counter is the position k)
+        Ufull = np.zeros((w.B, k + 1, w.V), np.float32)
+        Ufull[:, k] = w.U[:, k]
+        follow = np.zeros((w.B, k + 1), np.int32)
+        follow[:, k] = tok
+        if k > 0:
+            follow[:, k - 1] = prev
+        anchor = prev if k == 0 else np.zeros(w.B, np.int32)
+        ref = O.markov_draft(Ufull, w.W1, w.W2, anchor, mode=O.SAMPLE, seed=9, follow=follow)
+        sub = {key: v[:, k:k + 1] for key, v in ref.items()}
+        check_draft(tok[:, None], lp[:, None], sub)
+        agree = tok == sub["tokens"][:, 0]
+        assert np.abs(bl[agree] - ref["best_logit"][agree, k]).max() <= LOGIT_TOL
+
+
+def test_repeat_runs_bit_identical(D):
+    w = S.workload("serving", B=64, K=4, V=4096, r=256, mode=S.SAMPLE)
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    a = D.dspark_markov_draft(*args, mode=D.DSPARK_SAMPLE, seed=1)
+    b = D.dspark_markov_draft(*args, mode=D.DSPARK_SAMPLE, seed=1)
+    assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
+
+
+def test_k1_and_single_row(D):
+    w = S.strong("serving", B=1, K=1, V=31, r=16)
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, follow=tok)
+    check_draft(tok, lp, ref)
+
+
+# ------------------------------------------------------------------------------------------ full size
+
+@pytest.fixture(scope="module")
+def serving():
+    return S.workload("serving")
+
+
+def _full_draft_check(D, w, rows, mode, seed, H=None, Hd=None):
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), w2_layout=D.DSPARK_W2_VR,
+                                    H=H, mode=mode, seed=seed)
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2T, w.anchor, w2_layout=O.W2_VR, H=Hd, mode=mode, seed=seed, follow=tok,
+                         rows=rows)
+    sub = {k: v[rows] for k, v in ref.items()}
+    return check_draft(tok[rows], lp[rows], sub)
+
+
+def test_full_serving_sampled_rows(D, serving):
+    """B=128, K=16, V=151936, r=256, Gumbel-max T=1: every position of three sampled rows."""
+    _full_draft_check(D, serving, [0, 77, 127], S.SAMPLE, serving.noise_seed)
+
+
+def test_full_serving_logits_sampled_rows(D, serving):
+    w = serving
+    prev = w.anchor.copy()
+    for k in (0, w.K // 2, w.K - 1):
+        out = host(D.dspark_markov_logits(t_f32(w.U[:, k]), t_w(w.W1), t_w(w.W2T), t_i32(prev)))
+        rows = [3, 64, 126]
+        ref = O.markov_logits(w.U[:, k], w.W1, w.W2T, prev, w2_layout=O.W2_VR, rows=rows)
+        assert np.abs(out[rows] - ref[rows]).max() <= 1e-3
+        prev = (prev * 7 + 13) % w.V
+
+
+def test_full_batch1_greedy(D):
+    w = S.workload("batch1")
+    _full_draft_check(D, w, [0], S.GREEDY, 0)
