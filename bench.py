@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Throughput of the Markov-head draft round on one MI355X, with its roofline and a CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+
+A step is one draft round of the serving workload: B=128 rows, K=16 positions, vocabulary V=151936, rank
+r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, Gumbel-max sampling at T=1 with
+log-probabilities, i.e. dspark_markov_draft: for every position the fused bias-contraction / calibration
+/ pick kernel and the cross-workgroup reduction.  Inputs are synthetic (the seeded generator) and are
+resident in HBM before timing starts.  Before every timed round a 1 GiB fill evicts the L2 and the
+256 MB last-level cache, so the round starts with nothing of W2 or U cached; the fill is outside the
+event pair.  The printed line is one JSON object:
+
+    value          B*K / mean round time (draft tokens per second), from HIP events around each round
+    roofline       the fused step kernel against HBM bandwidth: algorithmic bytes of one launch (one
+                   position: W2 + U_k + gathered W1 rows + predecessors + outputs) over the kernel's mean
+                   duration, timed with HIP events on the library's stream around each launch
+    cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload, on this host's cores
+    extras         the other measured shapes (batch-1, top-16 Selector, gated head) and the back-to-back
+                   (no eviction) rate
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "calibrated draft tokens/s at B=128,K=16,V=151936,r=256; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "markov_step_serving_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rank_markov_draft_amd", "csrc", "markov.hip")
+
+
+def markov_bytes_per_position(B, V, r, gated=False):
+    """Algorithmic bytes of one position: W2 (bf16) + U_k (fp32) + gathered W1 rows (bf16) + predecessors
+    (int32) + token and log-probability outputs (+ gate rows, fp32)."""
+    return 2 * r * V + 4 * B * V + 2 * B * r + 4 * B + 8 * B + (4 * B * r if gated else 0)
+
+
+def selector_bytes_per_round(B, K, V, r, topk=16):
+    """U read once + gathered A/Bemb rows + candidate ids and values."""
+    return 4 * B * K * V + 2 * r * B * (K * topk + (K - 1) * topk + 1) + 8 * B * K * topk
+
+
+def source_hash():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def traffic_entry():
+    """Counter-measured HBM bytes per launch of the step kernel, if taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference kernel for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_markov_draft_amd as D
+    import synth as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+
+    def evict():
+        flush_buf.fill_(1)
+
+    def to_w(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed_rounds(fn, n, flush=True):
+        """Mean / p10 / p90 of n event-timed calls, each preceded by an (untimed) cache eviction."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            if flush:
+                evict()
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        return ms, wall
+
+    # ------------------------------------------------------------------ serving workload (the metric)
+    w = S.workload("serving")
+    B, K, V, r = w.B, w.K, w.V, w.r
+    U = torch.from_numpy(w.U).to(dev)
+    W1 = to_w(w.W1)
+    W2T = to_w(w.W2T)
+    anchor = torch.from_numpy(w.anchor).to(dev)
+    tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    logprobs = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(D.dspark_markov_workspace_bytes(B, K, V, r, D.DSPARK_BF16, D.DSPARK_W2_VR), dtype=torch.uint8,
+                     device=dev)
+
+    def serving_round():
+        D.dspark_markov_draft(U, W1, W2T, anchor, w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_SAMPLE, seed=w.noise_seed,
+                              temperature=w.temperature, tokens=tokens, logprobs=logprobs, workspace=ws)
+
+    for _ in range(args.warmup):
+        evict()
+        serving_round()
+    torch.cuda.synchronize()
+    ms, wall = timed_rounds(serving_round, args.steps)
+    ms_per_step = float(ms.mean())
+    value = B * K / (ms_per_step / 1e3)
+    bytes_pos = markov_bytes_per_position(B, V, r)
+    roof_round_ms = K * bytes_pos / (HBM_PEAK_GBS * 1e9) * 1e3
+    roof_tok_s = B * K / (roof_round_ms / 1e3)
+
+    # duration of the contraction kernel launches (events around each launch, on the library's stream)
+    kern_total, kern_launches, round_ms_timed = 0.0, 0, []
+    n_timed = max(3, min(args.steps, 10))
+    for _ in range(n_timed):
+        evict()
+        _, _, kms, nl, rms = D.dspark_markov_draft_timed(U, W1, W2T, anchor, w2_layout=D.DSPARK_W2_VR,
+                                                         mode=D.DSPARK_SAMPLE, seed=w.noise_seed,
+                                                         temperature=w.temperature, tokens=tokens, logprobs=logprobs,
+                                                         workspace=ws)
+        kern_total += kms
+        kern_launches += nl
+        round_ms_timed.append(rms)
+    kern_ms = kern_total / kern_launches
+    positions_per_launch = K * n_timed // kern_launches
+    bytes_launch = bytes_pos * positions_per_launch
+    achieved = bytes_launch / (kern_ms / 1e3) / 1e9
+    tr = traffic_entry()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if tr is None else tr["bytes_per_launch"],
+                "kernel": "markov_round_kernel<16, sample>" if positions_per_launch > 1 else "markov_step_mfma<16, sample>",
+                "bytes_per_launch": bytes_launch, "positions_per_launch": positions_per_launch,
+                "bytes_per_position": bytes_pos, "launch_ms_mean": round(kern_ms, 5)}
+
+    # back-to-back rounds without eviction (W2 may stay in the last-level cache across rounds)
+    ms_b2b, _ = timed_rounds(serving_round, args.steps, flush=False)
+
+    extras = {
+        "round_ms_p10": round(float(np.percentile(ms, 10)), 4), "round_ms_p90": round(float(np.percentile(ms, 90)), 4),
+        "pct_of_hbm_roofline": round(100.0 * roof_round_ms / ms_per_step, 2),
+        "roofline_tokens_per_s": round(roof_tok_s, 1), "roofline_round_ms": round(roof_round_ms, 4),
+        "back_to_back_round_ms": round(float(ms_b2b.mean()), 4),
+        "back_to_back_tokens_per_s": round(B * K / (float(ms_b2b.mean()) / 1e3), 1),
+        "timed_wall_s": round(wall, 4),
+    }
+    del U
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------------------------- other shapes
+    if not args.no_extras:
+        # greedy on the same serving shape
+        w = S.workload("serving", mode=S.GREEDY)
+        U = torch.from_numpy(w.U).to(dev)
+
+        def greedy_round():
+            D.dspark_markov_draft(U, W1, W2T, anchor, w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_GREEDY, tokens=tokens,
+                                  logprobs=logprobs, workspace=ws)
+
+        greedy_round()
+        gms, _ = timed_rounds(greedy_round, 10)
+        extras["serving_greedy"] = {"round_ms": round(float(gms.mean()), 4),
+                                    "tokens_per_s": round(B * K / (gms.mean() / 1e3), 1),
+                                    "pct_of_hbm_roofline": round(100.0 * roof_round_ms / float(gms.mean()), 2)}
+        del U
+        torch.cuda.empty_cache()
+
+        # top-16 Selector, ungated, greedy walk
+        w = S.workload("selector")
+        U = torch.from_numpy(w.U).to(dev)
+        A, Bemb = to_w(w.W1), to_w(w.W2T)
+        anc = torch.from_numpy(w.anchor).to(dev)
+        sws = torch.empty(D.dspark_selector_workspace_bytes(w.B, w.K, w.V, w.r, 16), dtype=torch.uint8, device=dev)
+
+        def sel_round():
+            D.dspark_selector_draft(U, A, Bemb, anc, topk=16, workspace=sws)
+
+        sel_round()
+        sms_, _ = timed_rounds(sel_round, 10)
+        sb = selector_bytes_per_round(w.B, w.K, w.V, w.r)
+        extras["selector_top16"] = {"round_ms": round(float(sms_.mean()), 4),
+                                    "tokens_per_s": round(w.B * w.K / (sms_.mean() / 1e3), 1),
+                                    "bytes_per_round": sb,
+                                    "pct_of_hbm_roofline": round(100.0 * sb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(sms_.mean()), 2)}
+        del U, A, Bemb
+        torch.cuda.empty_cache()
+
+        # gated head: gate GEMM for the block + gated full-vocabulary draft
+        w = S.workload("gated")
+        U = torch.from_numpy(w.U).to(dev)
+        W1g, W2g = to_w(w.W1), to_w(w.W2T)
+        h, Wg = to_w(w.h), to_w(w.Wg)
+        anc = torch.from_numpy(w.anchor).to(dev)
+        Hbuf = torch.empty((w.B, w.K, w.r), dtype=torch.float32, device=dev)
+        tok_g = torch.empty((w.B, w.K), dtype=torch.int32, device=dev)
+        lp_g = torch.empty((w.B, w.K), dtype=torch.float32, device=dev)
+        gws = torch.empty(D.dspark_markov_workspace_bytes(w.B, w.K, w.V, w.r, 1, 1), dtype=torch.uint8, device=dev)
+
+        def gated_round():
+            D.dspark_gate(h, Wg, out=Hbuf)
+            D.dspark_markov_draft(U, W1g, W2g, anc, H=Hbuf, tokens=tok_g, logprobs=lp_g, workspace=gws)
+
+        gated_round()
+        gms_, _ = timed_rounds(gated_round, 10)
+        gb = w.K * markov_bytes_per_position(w.B, w.V, w.r, gated=True) + 2 * w.B * w.K * w.D + 2 * w.D * w.r + 4 * w.B * w.K * w.r
+        extras["gated"] = {"round_ms": round(float(gms_.mean()), 4),
+                           "tokens_per_s": round(w.B * w.K / (gms_.mean() / 1e3), 1), "bytes_per_round": gb,
+                           "pct_of_hbm_roofline": round(100.0 * gb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gms_.mean()), 2)}
+        del U, W1g, W2g, h, Wg
+        torch.cuda.empty_cache()
+
+        # batch 1, greedy
+        w = S.workload("batch1")
+        U = torch.from_numpy(w.U).to(dev)
+        W1b, W2b = to_w(w.W1), to_w(w.W2T)
+        anc = torch.from_numpy(w.anchor).to(dev)
+        tok_b = torch.empty((1, w.K), dtype=torch.int32, device=dev)
+        lp_b = torch.empty((1, w.K), dtype=torch.float32, device=dev)
+        bws = torch.empty(D.dspark_markov_workspace_bytes(1, w.K, w.V, w.r, 1, 1), dtype=torch.uint8, device=dev)
+
+        def b1_round():
+            D.dspark_markov_draft(U, W1b, W2b, anc, tokens=tok_b, logprobs=lp_b, workspace=bws)
+
+        b1_round()
+        bms, _ = timed_rounds(b1_round, 10)
+        bb = w.K * markov_bytes_per_position(1, w.V, w.r)
+        extras["batch1"] = {"round_ms": round(float(bms.mean()), 4),
+                            "tokens_per_s": round(w.K / (bms.mean() / 1e3), 1), "bytes_per_round": bb,
+                            "pct_of_hbm_roofline": round(100.0 * bb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(bms.mean()), 2)}
+        del U, W1b, W2b
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+
+        w = S.workload("serving")
+        W2Th = w.W2T
+        t0 = time.perf_counter()
+        O.markov_draft(w.U, w.W1, W2Th, w.anchor, w2_layout=O.W2_VR, mode=O.SAMPLE, seed=w.noise_seed, rows=[0])
+        one = time.perf_counter() - t0
+        threads = O.num_threads()
+        nrows = int(max(1, min(w.B, round(args.cpu_seconds / max(one, 1e-3) * threads * 0.8))))
+        nrows = max(threads, nrows) if nrows < w.B else w.B
+        nrows = min(nrows, w.B)
+        rows = list(range(nrows))
+        t0 = time.perf_counter()
+        O.markov_draft(w.U, w.W1, W2Th, w.anchor, w2_layout=O.W2_VR, mode=O.SAMPLE, seed=w.noise_seed, rows=rows)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(nrows * w.K / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"serving workload rows 0..{nrows - 1} of {w.B}, all {w.K} positions, Gumbel-max T=1 "
+                         f"({nrows * w.K} draft tokens, fp64, {dt:.1f} s)"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "pct_of_roofline": extras["pct_of_hbm_roofline"], "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "serving: Markov-head draft round, Gumbel-max T=1, with log-probabilities",
+                   "B": B, "K": K, "V": V, "r": r, "weights": "bf16 (W2 stored [V, r])", "base_logits": "fp32",
+                   "accumulate": "fp32", "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

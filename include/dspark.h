@@ -114,6 +114,19 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement variant of dspark_markov_draft (same arguments and results).  It also records HIP event
+ * pairs on `stream` around every launch of the contraction kernel (one launch per round on the persistent
+ * path, one per position otherwise) and around the whole call, waits for the call to finish (this call
+ * synchronises the host with the stream), and writes to host memory: *kernel_ms, the summed duration of
+ * the contraction launches; *kernel_launches, their number; *round_ms, the whole call.  1 <= K <= 4096.
+ */
+int dspark_markov_draft_timed(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                              const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                              uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* workspace,
+                              size_t workspace_bytes, void* stream, float* kernel_ms, int* kernel_launches,
+                              float* round_ms);
+
+/*
  * One position of the same rule with the predecessors supplied by the caller (teacher forcing).
  * U_k      [B, V] fp32 with row b at U_k + b * u_stride (u_stride >= V).
  * prev     [B] int32 predecessors.   H_k: [B, r] fp32 or NULL.   k: the draft position, used only as the

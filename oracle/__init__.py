@@ -30,6 +30,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         i32, i64, u32, u64, dbl, vp = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64,
                                        ctypes.c_double, ctypes.c_void_p)
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = i32
         lib.oracle_fmix32.argtypes = [u32]
         lib.oracle_fmix32.restype = u32
         lib.oracle_noise_bits.argtypes = [u64, u32, u32, u32]
@@ -77,6 +79,11 @@ def _rows(rows: Optional[Sequence[int]]):
         return None, 0
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     return r, int(r.size)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 # --------------------------------------------------------------------------------------------- noise

@@ -34,6 +34,7 @@
  * closed form, a special case or brute force; see the test files.  No function here is unpinned.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -80,6 +81,9 @@ static uint32_t murmur3_fmix32(uint32_t h) {
 }
 
 uint32_t oracle_fmix32(uint32_t h) { return murmur3_fmix32(h); }
+
+/* Threads the parallel loops below use (OpenMP's current maximum). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* Chained key: k0 from the 64-bit seed, then the row, the position and the vocabulary id are
  * folded in one at a time, each followed by a full finalisation mix. */

@@ -42,6 +42,8 @@ def _load_lib():
         "dspark_last_error": ([], cp),
         "dspark_markov_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
         "dspark_markov_draft": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz, vp], i32),
+        "dspark_markov_draft_timed": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz,
+                                       vp, vp, vp, vp], i32),
         "dspark_markov_step": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp, sz,
                                 vp], i32),
         "dspark_markov_logits": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, sz, vp], i32),
@@ -137,6 +139,34 @@ def dspark_markov_draft(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mo
                                     float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb, _stream(stream)),
            "dspark_markov_draft")
     return tokens, logprobs
+
+
+def dspark_markov_draft_timed(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY, seed=0,
+                              temperature=1.0, tokens=None, logprobs=None, workspace=None, stream=None):
+    """dspark_markov_draft plus contraction-kernel timing (HIP events on the same stream).
+    Returns (tokens, logprobs, kernel_ms summed over the contraction launches, number of launches, round_ms)."""
+    _dev(U, "U", torch.float32, 3)
+    B, K, V = U.shape
+    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+    _dev(W2, "W2", W1.dtype, 2)
+    r = W1.shape[1]
+    _dev(anchor, "anchor", torch.int32, 1)
+    if H is not None:
+        _dev(H, "H", torch.float32, 3)
+    wd = _wdtype(W1)
+    if tokens is None:
+        tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
+    if logprobs is None:
+        logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device)
+    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+    kernel_ms = ctypes.c_float()
+    launches = ctypes.c_int()
+    round_ms = ctypes.c_float()
+    _check(_lib.dspark_markov_draft_timed(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r, mode,
+                                          seed, float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb,
+                                          _stream(stream), ctypes.byref(kernel_ms), ctypes.byref(launches),
+                                          ctypes.byref(round_ms)), "dspark_markov_draft_timed")
+    return tokens, logprobs, float(kernel_ms.value), int(launches.value), float(round_ms.value)
 
 
 def dspark_markov_step(U_k, W1, W2, prev, k, *, w2_layout=DSPARK_W2_VR, H_k=None, mode=DSPARK_GREEDY, seed=0,

@@ -2,6 +2,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "../../include/dspark.h"
 #include "internal.hpp"
@@ -32,21 +33,42 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 struct MarkovWs {
-    Partials part;
+    Partials part;  // per-step path: [kMaxG][Bpad]
     int Bpad;
+    unsigned long long* winners;  // whole-round path
+    uint32_t* counters;
+    float* p_mc;
+    float* p_s;
+    int* p_idx;
+    float* p_l;
     void* w2t;  // transposed W2 (only when an [r, V] bf16 W2 is drafted on the matrix-core path)
 };
 
 bool mfma_eligible(int wdtype, int r) { return wdtype == DSPARK_BF16 && mfma_supported_r(r); }
 
-size_t markov_ws_bytes(int B, int V, int r, int wdtype, int w2_layout, bool need_pack) {
+size_t step_part_bytes(int B) { return 5 * align256(sizeof(float) * kMaxG * (size_t)round_up(B, kRowPad)); }
+
+int round_gmax() {
+    const int n = device_cu_count();
+    return n < kMaxG ? n : kMaxG;
+}
+
+constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines) and the error word
+
+// winners [K][Bpad] u64, the counters, four [K][Gmax][Bpad] partial arrays
+size_t round_region_bytes(int B, int K) {
     const size_t Bpad = (size_t)round_up(B, kRowPad);
-    size_t bytes = 5 * align256(sizeof(float) * kMaxG * Bpad);
+    return align256(sizeof(unsigned long long) * (size_t)K * Bpad) + kCounterBytes +
+           4 * align256(sizeof(float) * (size_t)K * round_gmax() * Bpad);
+}
+
+size_t markov_ws_bytes(int B, int K, int V, int r, int wdtype, int w2_layout, bool need_pack) {
+    size_t bytes = step_part_bytes(B) + round_region_bytes(B, K);
     if (need_pack && w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) bytes += align256((size_t)V * r * 2);
     return bytes;
 }
 
-MarkovWs carve_markov(void* ws, int B) {
+MarkovWs carve_markov(void* ws, int B, int K) {
     MarkovWs w{};
     w.Bpad = round_up(B, kRowPad);
     uint8_t* p = (uint8_t*)ws;
@@ -56,7 +78,17 @@ MarkovWs carve_markov(void* ws, int B) {
     w.part.l = (float*)(p + 2 * one);
     w.part.m = (float*)(p + 3 * one);
     w.part.s = (float*)(p + 4 * one);
-    w.w2t = p + 5 * one;
+    uint8_t* q = p + 5 * one;
+    const size_t wn = align256(sizeof(unsigned long long) * (size_t)K * w.Bpad);
+    w.winners = (unsigned long long*)q;
+    w.counters = (uint32_t*)(q + wn);
+    const size_t pn = align256(sizeof(float) * (size_t)K * round_gmax() * w.Bpad);
+    uint8_t* pp = q + wn + kCounterBytes;
+    w.p_mc = (float*)pp;
+    w.p_s = (float*)(pp + pn);
+    w.p_idx = (int*)(pp + 2 * pn);
+    w.p_l = (float*)(pp + 3 * pn);
+    w.w2t = pp + 4 * pn;
     return w;
 }
 
@@ -77,7 +109,8 @@ int check_common(const void* W1, const void* W2, int wdtype, int w2_layout, int 
 int run_step(const float* Uk, int64_t u_stride, const void* W1, const void* W2, int wdtype, int w2_layout,
              const int32_t* prev, int64_t prev_stride, const float* Hk, int64_t h_stride, int B, int V, int r, int k,
              int mode, uint32_t k0, float temperature, int32_t* tok, float* lp, float* bestl, int64_t out_stride,
-             const MarkovWs* ws, float* logits_out, hipStream_t st) {
+             const MarkovWs* ws, float* logits_out, hipStream_t st, hipEvent_t ev_begin = nullptr,
+             hipEvent_t ev_end = nullptr) {
     const bool store = logits_out != nullptr;
     const int kmode = store ? kModeStore : (mode == DSPARK_SAMPLE ? kModeSample : kModeGreedy);
     const float teff = (mode == DSPARK_SAMPLE) ? temperature : 1.0f;
@@ -117,7 +150,9 @@ int run_step(const float* Uk, int64_t u_stride, const void* W1, const void* W2, 
         G = a.ntiles < ncu * kMfmaWGPerCU ? a.ntiles : ncu * kMfmaWGPerCU;
         if (G > kMaxG) G = kMaxG;
         const bool vec_u = (V % 4 == 0) && (u_stride % 4 == 0) && aligned16(Uk);
+        if (ev_begin) (void)hipEventRecord(ev_begin, st);
         e = launch_markov_step_mfma(a, kmode, gated, vec_u, G, st);
+        if (ev_end) (void)hipEventRecord(ev_end, st);
     } else {
         StepArgsValu a{};
         a.U = Uk;
@@ -142,7 +177,9 @@ int run_step(const float* Uk, int64_t u_stride, const void* W1, const void* W2, 
         const int nblk = (V + 255) / 256;
         G = nblk < ncu * 4 ? nblk : ncu * 4;
         if (G > kMaxG) G = kMaxG;
+        if (ev_begin) (void)hipEventRecord(ev_begin, st);
         e = launch_markov_step_valu(a, wdtype == DSPARK_BF16, kmode, gated, G, st);
+        if (ev_end) (void)hipEventRecord(ev_end, st);
     }
     if (e != hipSuccess) return device_fail(e, "markov step launch");
     if (store) return DSPARK_OK;
@@ -157,6 +194,99 @@ int run_step(const float* Uk, int64_t u_stride, const void* W1, const void* W2, 
     ra.out_stride = out_stride;
     e = launch_markov_reduce(ra, B, st);
     if (e != hipSuccess) return device_fail(e, "markov reduce launch");
+    return DSPARK_OK;
+}
+
+bool coop_supported() {
+    static int cached[64] = {0};  // 0 unknown, 1 yes, 2 no
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (cached[dev] == 0) {
+        int v = 0;
+        cached[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && v) ? 1 : 2;
+    }
+    return cached[dev] == 1;
+}
+
+int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout, const int32_t* anchor,
+                      const float* H, int B, int K, int V, int r, int mode, uint64_t seed, float temperature,
+                      int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes, void* stream,
+                      hipEvent_t* ev, int* kernel_launches) {
+    g_err[0] = 0;
+    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
+    if (rc) return rc;
+    if (!U || !anchor || !tokens) return fail(DSPARK_EINVAL, "U, anchor and tokens must not be NULL");
+    if (K <= 0) return fail(DSPARK_EINVAL, "K must be positive");
+    if (B > 65535) return fail(DSPARK_EUNSUPPORTED, "B = %d too large for a draft", B);
+    const size_t need = markov_ws_bytes(B, K, V, r, wdtype, w2_layout, true);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    MarkovWs ws = carve_markov(workspace, B, K);
+    const void* W2use = W2;
+    int layout = w2_layout;
+    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {
+        hipError_t e = launch_transpose(W2, r, V, 2, ws.w2t, st);
+        if (e != hipSuccess) return device_fail(e, "transpose launch");
+        W2use = ws.w2t;
+        layout = DSPARK_W2_VR;
+    }
+    const uint32_t k0 = noise_key0(seed);
+    const bool sample = mode == DSPARK_SAMPLE;
+    const float teff = sample ? temperature : 1.0f;
+
+    // whole round in one persistent launch when the shape allows it
+    const bool round_ok = mfma_eligible(wdtype, r) && round_supported_r(r) && layout == DSPARK_W2_VR && aligned16(W1) && aligned16(W2use) &&
+                          aligned16(U) && V % 4 == 0 && (!H || aligned16(H)) && coop_supported();
+    if (round_ok) {
+        const int ntiles = (V + 31) / 32;
+        int G = round_max_coresident(r, sample, H != nullptr);
+        if (G > round_gmax()) G = round_gmax();
+        if (G > ntiles) G = ntiles;
+        if (G >= 1) {
+            RoundArgs a{};
+            a.U = U;
+            a.u_stride = (int64_t)K * V;
+            a.u_kstride = V;
+            a.W1 = (const uint16_t*)W1;
+            a.W2t = (const uint16_t*)W2use;
+            a.anchor = anchor;
+            a.H = H;
+            a.B = B;
+            a.K = K;
+            a.V = V;
+            a.r = r;
+            a.k0 = k0;
+            a.c = kLog2e / teff;
+            a.ntiles = ntiles;
+            a.G = G;
+            a.Bpad = ws.Bpad;
+            a.winners = ws.winners;
+            a.barrier = ws.counters;
+            a.error = ws.counters + 256;  // after the 8 counter lines (32 words apart)
+            a.spin_limit = 1u << 22;
+            a.p_mc = ws.p_mc;
+            a.p_s = ws.p_s;
+            a.p_idx = ws.p_idx;
+            a.p_l = ws.p_l;
+            hipError_t e = launch_markov_round(a, sample, H != nullptr, tokens, logprobs, 1.0f / teff, st,
+                                               ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+            if (e != hipSuccess) return device_fail(e, "draft round launch");
+            if (kernel_launches) *kernel_launches = 1;
+            return DSPARK_OK;
+        }
+    }
+    // one launch pair (contraction, reduction) per position
+    for (int k = 0; k < K; ++k) {
+        const int32_t* prev = (k == 0) ? anchor : tokens + (k - 1);
+        const int64_t pstride = (k == 0) ? 1 : K;
+        rc = run_step(U + (size_t)k * V, (int64_t)K * V, W1, W2use, wdtype, layout, prev, pstride,
+                      H ? H + (size_t)k * r : nullptr, (int64_t)K * r, B, V, r, k, mode, k0, temperature, tokens + k,
+                      logprobs ? logprobs + k : nullptr, nullptr, K, &ws, nullptr, st, ev ? ev[2 * k] : nullptr,
+                      ev ? ev[2 * k + 1] : nullptr);
+        if (rc) return rc;
+    }
+    if (kernel_launches) *kernel_launches = K;
     return DSPARK_OK;
 }
 
@@ -184,7 +314,7 @@ const char* dspark_last_error(void) { return g_err; }
 
 size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int w2_layout) {
     if (B <= 0 || K <= 0 || V <= 0 || r <= 0) return 0;
-    return markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
+    return markov_ws_bytes(B, K, V, r, wdtype, w2_layout, true);
 }
 
 int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, void* stream) {
@@ -201,34 +331,50 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode, uint64_t seed,
                         float temperature, int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes,
                         void* stream) {
+    return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
+                             logprobs, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dspark_markov_draft_timed(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                              const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                              uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* workspace,
+                              size_t workspace_bytes, void* stream, float* kernel_ms, int* kernel_launches,
+                              float* round_ms) {
     g_err[0] = 0;
-    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
-    if (rc) return rc;
-    if (!U || !anchor || !tokens) return fail(DSPARK_EINVAL, "U, anchor and tokens must not be NULL");
-    if (K <= 0) return fail(DSPARK_EINVAL, "K must be positive");
-    const size_t need = markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
-    if (!workspace || workspace_bytes < need)
-        return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (!kernel_ms || !kernel_launches || !round_ms) return fail(DSPARK_EINVAL, "timing outputs must not be NULL");
+    if (K <= 0 || K > 4096) return fail(DSPARK_EINVAL, "K must be in [1, 4096] for the timed call");
+    std::vector<hipEvent_t> ev(2 * (size_t)K + 2, nullptr);
+    for (auto& x : ev) {
+        hipError_t e = hipEventCreate(&x);
+        if (e != hipSuccess) {
+            for (auto& y : ev)
+                if (y) (void)hipEventDestroy(y);
+            return device_fail(e, "hipEventCreate");
+        }
+    }
     hipStream_t st = (hipStream_t)stream;
-    MarkovWs ws = carve_markov(workspace, B);
-    const void* W2use = W2;
-    int layout = w2_layout;
-    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {
-        hipError_t e = launch_transpose(W2, r, V, 2, ws.w2t, st);
-        if (e != hipSuccess) return device_fail(e, "transpose launch");
-        W2use = ws.w2t;
-        layout = DSPARK_W2_VR;
+    (void)hipEventRecord(ev[2 * K], st);
+    int launches = 0;
+    int rc = markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
+                               logprobs, workspace, workspace_bytes, stream, ev.data(), &launches);
+    (void)hipEventRecord(ev[2 * K + 1], st);
+    if (rc == DSPARK_OK) {
+        hipError_t e = hipEventSynchronize(ev[2 * K + 1]);
+        if (e != hipSuccess) rc = device_fail(e, "hipEventSynchronize");
     }
-    const uint32_t k0 = noise_key0(seed);
-    for (int k = 0; k < K; ++k) {
-        const int32_t* prev = (k == 0) ? anchor : tokens + (k - 1);
-        const int64_t pstride = (k == 0) ? 1 : K;
-        rc = run_step(U + (size_t)k * V, (int64_t)K * V, W1, W2use, wdtype, layout, prev, pstride,
-                      H ? H + (size_t)k * r : nullptr, (int64_t)K * r, B, V, r, k, mode, k0, temperature, tokens + k,
-                      logprobs ? logprobs + k : nullptr, nullptr, K, &ws, nullptr, st);
-        if (rc) return rc;
+    if (rc == DSPARK_OK) {
+        float total = 0.f;
+        for (int i = 0; i < launches; ++i) {
+            float t = 0.f;
+            (void)hipEventElapsedTime(&t, ev[2 * i], ev[2 * i + 1]);
+            total += t;
+        }
+        *kernel_ms = total;
+        *kernel_launches = launches;
+        (void)hipEventElapsedTime(round_ms, ev[2 * K], ev[2 * K + 1]);
     }
-    return DSPARK_OK;
+    for (auto& x : ev) (void)hipEventDestroy(x);
+    return rc;
 }
 
 int dspark_markov_step(const float* U_k, int64_t u_stride, const void* W1, const void* W2, int wdtype, int w2_layout,
@@ -241,11 +387,11 @@ int dspark_markov_step(const float* U_k, int64_t u_stride, const void* W1, const
     if (!U_k || !prev || !tok) return fail(DSPARK_EINVAL, "U_k, prev and tok must not be NULL");
     if (u_stride < V) return fail(DSPARK_EINVAL, "u_stride %lld < V %d", (long long)u_stride, V);
     if (k < 0) return fail(DSPARK_EINVAL, "k must be >= 0");
-    const size_t need = markov_ws_bytes(B, V, r, wdtype, w2_layout, true);
+    const size_t need = markov_ws_bytes(B, 1, V, r, wdtype, w2_layout, true);
     if (!workspace || workspace_bytes < need)
         return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     hipStream_t st = (hipStream_t)stream;
-    MarkovWs ws = carve_markov(workspace, B);
+    MarkovWs ws = carve_markov(workspace, B, 1);
     const void* W2use = W2;
     int layout = w2_layout;
     if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r)) {

@@ -60,6 +60,33 @@ struct ReduceArgs {
     int64_t out_stride;
 };
 
+// A whole draft round in one persistent cooperative launch (bf16, W2 stored [V, r], V % 4 == 0).
+struct RoundArgs {
+    const float* U;             // U[b, k, v] at U + k * u_kstride + b * u_stride + v
+    int64_t u_stride, u_kstride;
+    const uint16_t* W1;         // [V, r]
+    const uint16_t* W2t;        // [V, r]
+    const int32_t* anchor;      // [B]
+    const float* H;             // [B, K, r] or null
+    int B, K, V, r;
+    uint32_t k0;
+    float c;                    // log2(e) / T
+    int ntiles, G, Bpad;
+    unsigned long long* winners;  // [K][Bpad] packed (ordered key, ~id)
+    uint32_t* barrier;          // grid barrier counter
+    uint32_t* error;            // set if a barrier wait timed out
+    uint32_t spin_limit;
+    float* p_mc;                // [K][G][Bpad] log-sum-exp partials (base-2 max of l c, sum)
+    float* p_s;
+    int* p_idx;                 // [K][G][Bpad] best id and its logit per workgroup
+    float* p_l;
+};
+int round_supported_r(int r);
+int round_lds_bytes(int r);
+int round_max_coresident(int r, bool sample, bool gated);
+hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, int32_t* tokens, float* logprobs,
+                               float inv_t, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+
 int mfma_supported_r(int r);
 hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);
 hipError_t launch_markov_step_valu(const StepArgsValu& a, bool bf16, int mode, bool gated, int G, hipStream_t st);

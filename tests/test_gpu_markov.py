@@ -29,14 +29,19 @@ def _rand_H(B, K, r, seed=0):
     return np.random.default_rng(seed).uniform(0.0, 1.0, (B, K, r)).astype(np.float32)
 
 
-# (B, K, V, r, wdtype): tile-spanning small shapes; r=24 and r=48 take the vector-ALU path
+# (B, K, V, r, wdtype): tile-spanning small shapes.  bf16 with r a power-of-two multiple of 16 and V % 4 == 0
+# drafts with the persistent whole-round kernel; V % 4 != 0 with the per-position kernels; r=24 and r=48 and
+# fp32 weights take the vector-ALU path
 SHAPES = [
     (1, 4, 512, 16, S.F32),
+    (3, 3, 1000, 16, S.BF16),
+    (130, 2, 776, 32, S.BF16),
+    (128, 3, 4096, 256, S.BF16),
     (5, 3, 1000, 64, S.BF16),
     (130, 2, 777, 32, S.BF16),
     (3, 3, 100, 24, S.BF16),
     (4, 2, 600, 48, S.BF16),
-    (2, 2, 300, 512, S.BF16),
+    (2, 2, 300, 512, S.BF16),  # r = 512: per-position kernels
     (7, 2, 257, 16, S.F32),
 ]
 
