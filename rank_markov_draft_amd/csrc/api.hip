@@ -55,10 +55,10 @@ int round_gmax() {
 
 constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines) and the error word
 
-// winners [K][Bpad] u64, the counters, four [K][Gmax][Bpad] partial arrays
+// winners [K][Bpad] u64 (kWinnerStride words apart), the counters, four [K][Gmax][Bpad] partial arrays
 size_t round_region_bytes(int B, int K) {
     const size_t Bpad = (size_t)round_up(B, kRowPad);
-    return align256(sizeof(unsigned long long) * (size_t)K * Bpad) + kCounterBytes +
+    return align256(sizeof(unsigned long long) * (size_t)K * Bpad * kWinnerStride) + kCounterBytes +
            4 * align256(sizeof(float) * (size_t)K * round_gmax() * Bpad);
 }
 
@@ -79,7 +79,7 @@ MarkovWs carve_markov(void* ws, int B, int K) {
     w.part.m = (float*)(p + 3 * one);
     w.part.s = (float*)(p + 4 * one);
     uint8_t* q = p + 5 * one;
-    const size_t wn = align256(sizeof(unsigned long long) * (size_t)K * w.Bpad);
+    const size_t wn = align256(sizeof(unsigned long long) * (size_t)K * w.Bpad * kWinnerStride);
     w.winners = (unsigned long long*)q;
     w.counters = (uint32_t*)(q + wn);
     const size_t pn = align256(sizeof(float) * (size_t)K * round_gmax() * w.Bpad);

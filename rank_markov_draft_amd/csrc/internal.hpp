@@ -72,7 +72,7 @@ struct RoundArgs {
     uint32_t k0;
     float c;                    // log2(e) / T
     int ntiles, G, Bpad;
-    unsigned long long* winners;  // [K][Bpad] packed (ordered key, ~id)
+    unsigned long long* winners;  // [K][Bpad] packed (ordered key, ~id), kWinnerStride words apart
     uint32_t* barrier;          // grid barrier counter
     uint32_t* error;            // set if a barrier wait timed out
     uint32_t spin_limit;
@@ -81,6 +81,9 @@ struct RoundArgs {
     int* p_idx;                 // [K][G][Bpad] best id and its logit per workgroup
     float* p_l;
 };
+// Each (position, row) winner word has a 128-byte line of its own: every workgroup updates every row's word
+// once per position, and words sharing a line would serialise those atomics.
+constexpr int kWinnerStride = 16;
 int round_supported_r(int r);
 int round_lds_bytes(int r);
 int round_max_coresident(int r, bool sample, bool gated);

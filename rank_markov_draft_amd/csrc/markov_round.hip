@@ -7,24 +7,28 @@
 // normalization has to be local").
 //
 // Design (gfx950):
-//  * One workgroup per CU, co-resident (cooperative launch).  Workgroup g owns a fixed contiguous range of
-//    32-wide vocabulary tiles for the whole round; wave w owns batch rows 32w .. 32w+31 of each 128-row block.
+//  * One workgroup per CU, co-resident (cooperative launch).  Workgroup g owns the 32-wide vocabulary tiles
+//    g, g + G, g + 2G, ... for the whole round; wave w owns batch rows 32w .. 32w+31 of each 128-row block.
 //  * Four producer waves stream W2 tiles ([32, r] bf16 rows of the [V, r] layout) and U tiles ([128, 32] fp32)
 //    with ordinary 16-byte vector loads (kDepth items ahead in registers; on this part they sustain more
 //    bandwidth than direct global->LDS loads) into a ring of kNS LDS stages; four consumer waves compute.
 //    Producers and consumers hand stages over through LDS counters, with no workgroup barrier per tile.
-//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries.  Stage
-//    layouts are XOR-swizzled (and skewed every 8 U rows) so the MFMA operand reads are bank-conflict free.
-//  * Per tile: C[v, b] = sum_j W2t[v, j] X[b, j] with v_mfma_f32_32x32x16_bf16 (A = W2 tile from LDS,
-//    B = the gathered predecessor rows X, resident in registers for the position).  A lane holds one batch
-//    row and 16 vocabulary ids of the accumulator; calibration, the streaming log-sum-exp and the running
-//    pick are per-lane scalars.  No logits are written.
+//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries (a few
+//    items: the boundary itself is latency-bound).  Stage rows are padded by 16 bytes, so the 16-byte operand
+//    reads of 8 consecutive lanes fall in distinct banks and use immediate offsets.
+//  * Per tile: C[v, b] = U[b, v] + sum_j W2t[v, j] X[b, j] with v_mfma_f32_32x32x16_bf16 (A = W2 tile from
+//    LDS, stored in permuted row slots; B = the gathered predecessor rows X, resident in registers for the
+//    position; C seeded with the U tile).  A lane holds one batch row and 16 consecutive vocabulary ids of
+//    the accumulator; calibration, the streaming log-sum-exp and the running pick are per-lane scalars.  The
+//    MFMAs of tile t + 1 are issued inside the epilogue of tile t.  No logits are written.
 //  * Sampling uses the exponential-race form of Gumbel-max: argmax_v p_v / E_v with p_v = 2^(l_v c - m) (the
 //    same exponential the log-sum-exp needs) and E_v = -log2 u_v, which is argmax_v (l_v / T + G_v) exactly.
 //  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id) gives the global
 //    pick with ties to the lower id; log-sum-exp partials go to the workspace.  A grid barrier (counter,
 //    bounded spin) then releases the next position, whose workgroups gather W1 rows of the new tokens.
 //  * A finalize kernel merges the log-sum-exp partials of all positions into tokens and log-probabilities.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -32,26 +36,30 @@ namespace dspark {
 
 namespace {
 
-constexpr int kRThreads = 256;
 constexpr int kRTileV = 32;
 constexpr int kRRows = 128;
-constexpr int kUGroupBytes = 8 * 128 + 16;  // 8 U rows of 32 floats + 16-byte skew
-constexpr float kNegBig = -1e30f;          // start of a running max; stays finite when scaled by log2(e)/T
+constexpr float kNegBig = -1e30f;  // start of a running max; stays finite when scaled by log2(e)/T
 
 template <int RK>
 struct Ring {
     static constexpr int kNS = 4;
-    static constexpr int kRowBytes = 32 * RK;                 // one W2 row: r = 16 RK bf16
-    static constexpr int kW2Bytes = kRTileV * kRowBytes;      // 32 rows
-    static constexpr int kUBytes = 16 * kUGroupBytes;         // 128 rows in 16 skewed groups of 8
+    static constexpr int kW2Row = 32 * RK + 16;            // one W2 row (r = 16 RK bf16) + 16-byte pad
+    static constexpr int kW2Bytes = kRTileV * kW2Row;      // 32 rows
+    static constexpr int kURow = 4 * kRTileV + 16;          // one U row of the tile (32 floats) + 16-byte pad
+    static constexpr int kUBytes = kRRows * kURow;          // 128 rows
     static constexpr int kStage = kW2Bytes + kUBytes;
-    static constexpr int kSwz = ((2 * RK < 16) ? 2 * RK : 16) - 1;
     // one item = RK W2 units (64 lanes x 16 B) + 16 U units (8 rows x 128 B); producer p takes units p, p + 4, ...
     static constexpr int kUnits = RK + 16;
     static constexpr int kUnitsPerProducer = (kUnits + 3) / 4;
-    static constexpr int kDepth = 3;                          // items in flight per producer, in registers
+    static constexpr int kDepth = 3;                        // items in flight per producer, in registers
 };
 
+// Row rho of a W2 tile (vocabulary id v0 + rho) is stored in LDS slot w2_slot(rho).  MFMA A-operand row m
+// (read by lanes m and m + 32) produces accumulator rows 8 (i / 4) + 4 (lane / 32) + i % 4, so with this
+// order accumulator i of a lane holds id v0 + 16 (lane / 32) + i: 16 consecutive ids per lane.
+__device__ __forceinline__ int w2_slot(int rho) { return 8 * ((rho & 15) >> 2) + 4 * (rho >> 4) + (rho & 3); }
+
+constexpr int kGateItems = 4;  // items of the next position that may be in flight at a position boundary
 constexpr int kConsumers = 4;
 constexpr int kProducers = 4;
 constexpr int kRoundThreads = 64 * (kConsumers + kProducers);
@@ -97,9 +105,11 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     const int G = gridDim.x;
     const int g = blockIdx.x;
     const int r = 16 * RK;
-    const int t0 = (int)(((long long)g * a.ntiles) / G);
-    const int t1 = (int)(((long long)(g + 1) * a.ntiles) / G);
-    const int ntw = t1 - t0;
+    // Tiles are dealt out cyclically: workgroup g takes tiles g, g + G, g + 2G, ...  At any moment the
+    // workgroups then read neighbouring 128-byte pieces of each U row (and one contiguous W2 span), which
+    // keeps the HBM row buffers open, where contiguous blocks of tiles per workgroup would scatter the reads.
+    const int ntw = (a.ntiles - g + G - 1) / G;
+    auto tile_of = [&](int j) { return g + G * j; };
     const int nrb = (a.B + kRRows - 1) / kRRows;
     const int per_k = nrb * ntw;
     const int nitems = a.K * per_k;
@@ -117,7 +127,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
 
     if (wave >= kConsumers) {
         // ============================================================== producers: stream W2 and U tiles
-        // Ordinary 16-byte vector loads into registers, kDepth items ahead, then ds_write into the swizzled
+        // Ordinary 16-byte vector loads into registers, kDepth items ahead, then ds_write into the padded
         // stage layout the consumers read.  Unit u of an item: u < RK is W2 rows 2u .. (64 lanes x 16 B of the
         // tile's [32, r] block); u >= RK is U row group u - RK (8 rows x 32 floats).
         const int p = wave - kConsumers;
@@ -128,7 +138,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             const int k = i / per_k;
             const int rem = i - k * per_k;
             const int rb = rem / ntw;
-            const int t = t0 + (rem - rb * ntw);
+            const int t = tile_of(rem - rb * ntw);
             const int v0 = t * kRTileV;
             const float* ub = a.U + (size_t)k * a.u_kstride;
 #pragma unroll
@@ -138,7 +148,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                     const int P = u * 64 + lane;
                     const int rho = P / (2 * RK), c = P % (2 * RK);
                     const int vrow = min(v0 + rho, a.V - 1);
-                    dst[n] = load_nt_u32x4(a.W2t + (size_t)vrow * r + 8 * c);
+                    // W2 is re-read every position: a cacheable load lets it stay in the last-level cache
+                    dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * c);
                 } else if (u < RG::kUnits) {
                     const int q = u - RK;
                     const int b = min(rb * kRRows + q * 8 + (lane >> 3), a.B - 1);
@@ -155,11 +166,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 if (u < RK) {
                     const int P = u * 64 + lane;
                     const int rho = P / (2 * RK), c = P % (2 * RK);
-                    *reinterpret_cast<u32x4_t*>(st + rho * RG::kRowBytes + 16 * (c ^ (rho & RG::kSwz))) = src[n];
+                    *reinterpret_cast<u32x4_t*>(st + w2_slot(rho) * RG::kW2Row + 16 * c) = src[n];
                 } else if (u < RG::kUnits) {
                     const int q = u - RK;
-                    const int rho8 = lane >> 3, c = lane & 7;
-                    *reinterpret_cast<u32x4_t*>(st + RG::kW2Bytes + q * kUGroupBytes + rho8 * 128 + 16 * (c ^ rho8)) = src[n];
+                    *reinterpret_cast<u32x4_t*>(st + RG::kW2Bytes + (8 * q + (lane >> 3)) * RG::kURow + 16 * (lane & 7)) = src[n];
                 }
             }
         };
@@ -179,6 +189,25 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             wait_lgkmcnt0();
             if (lane == 0) lds_add(&ready[i % RG::kNS], 1u);
         };
+        // A position's items past its first kGateItems are not loaded before the consumers have started that
+        // position.  The boundary between positions is a chain of latency-bound memory operations (pick
+        // atomics, barrier polls, the gather of the new rows) that queue behind this CU's outstanding vector
+        // loads, so only a few items may be in flight while it runs.
+        // The gate sits between publish(i) and load(i + D): blocking there must not hold back an item of the
+        // previous position, so at least the first D - 1 items of a position pass.
+        static_assert(kGateItems >= RG::kDepth - 1, "the load gate would block items the consumers wait for");
+        auto gate = [&](int j) {
+            const int kj = j / per_k;
+            if (kj == 0 || j - kj * per_k < kGateItems) return;
+            uint32_t spins = 0;
+            while (lds_load(&released) < (uint32_t)kj) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins > spin_limit) {
+                    __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        };
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (d < nitems) load(d, regs[d]);
@@ -188,7 +217,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 const int i = i0 + d;
                 if (i < nitems) {
                     publish(i, regs[d]);
-                    if (i + D < nitems) load(i + D, regs[d]);
+                    if (i + D < nitems) {
+                        gate(i + D);
+                        load(i + D, regs[d]);
+                    }
                 }
             }
         }
@@ -198,13 +230,15 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     // ================================================================== consumers: contraction and pick
     bf16x8_t xf[RK];
     uint32_t k2 = 0;
-    float m = kNegBig, s = 0.f;      // running max of l (natural units) and sum of 2^(l c - m c)
-    float bp = 0.f, bE = 1.f;        // sampling: best p = 2^(l c - m c) and its E = -log2 u
-    float bl = -INFINITY;            // greedy: best logit
-    int bi = 0x7FFFFFFF;
+    float m = kNegBig, s = 0.f;  // running max of l (natural units) and sum of 2^(l c - m c)
+    float bp = 0.f, bE = 1.f;    // sampling: best p = 2^(l c - m c) and its E = -log2 u
+    float bl = -INFINITY;        // greedy: best logit
+    int bslot = 0, btile = -1;   // best id = 32 btile + 16 half + bslot
     const float c = a.c;
     const int rho = lane & 31;
-    const int rr = wave * 32 + rho;  // this lane's row inside the 128-row block
+    const int rr = wave * 32 + rho;                                      // this lane's row of the 128-row block
+    const int a_off = rho * RG::kW2Row + 16 * half;                      // its A-operand row in a stage
+    const int u_off = RG::kW2Bytes + rr * RG::kURow + 64 * half;        // its 16 U values in a stage
 
     auto wait_ready = [&](int i) {
         const uint32_t need = (uint32_t)kProducers * (uint32_t)(i / RG::kNS + 1);
@@ -216,101 +250,110 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 break;
             }
         }
+        __asm__ volatile("" ::: "memory");  // stage reads stay after the wait
     };
-    // MFMA over the rank for stage i; the operand reads are issued in batches of up to 16 so their
-    // LDS latency overlaps, then the MFMAs run back to back.  U values of the lane's row go to u.
-    constexpr int kBatch = RK < 16 ? RK : 16;
-    auto stage_mma = [&](int i, f32x16_t& acc, float (&u)[16]) {
-        const uint8_t* st = ring + (i % RG::kNS) * RG::kStage;
-        const uint8_t* arow = st + rho * RG::kRowBytes;
-        const uint8_t* urow = st + RG::kW2Bytes + (rr >> 3) * kUGroupBytes + (rr & 7) * 128;
-        f32x4_t u4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) u4[q] = *reinterpret_cast<const f32x4_t*>(urow + 16 * ((2 * q + half) ^ (rr & 7)));
-        acc = f32x16_t{};
-#pragma unroll
-        for (int k0 = 0; k0 < RK; k0 += kBatch) {
-            bf16x8_t af[kBatch];
-#pragma unroll
-            for (int kk = 0; kk < kBatch; ++kk)
-                af[kk] = *reinterpret_cast<const bf16x8_t*>(arow + 16 * ((2 * (k0 + kk) + half) ^ (rho & RG::kSwz)));
-#pragma unroll
-            for (int kk = 0; kk < kBatch; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], xf[k0 + kk], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u[4 * q + 0] = u4[q].x;
-            u[4 * q + 1] = u4[q].y;
-            u[4 * q + 2] = u4[q].z;
-            u[4 * q + 3] = u4[q].w;
-        }
+    auto release = [&](int i) {
+        wait_lgkmcnt0();
+        __asm__ volatile("" ::: "memory");  // and before the release
+        if (lane == 0) lds_add(&freed[i % RG::kNS], 1u);
     };
-    // calibration, streaming log-sum-exp and running pick over the 16 ids of one tile
-    auto epilogue = [&](const f32x16_t& acc, const float (&u)[16], int t) {
-        const int v0 = t * kRTileV;
-        const int vl = v0 + 4 * half;  // id of slot i2 = vl + 8 (i2 / 4) + i2 % 4
-        float E[16];
-        if (SAMPLE) {
-            // noise first: it does not depend on the contraction.  fmix32(k2 ^ v) for the ids vl + 8q + o,
-            // o = 0..3 (vl + 8q is a multiple of 4, so k2 ^ (vl + 8q + o) = (k2 ^ (vl + 8q)) ^ o and the first
-            // xor-shift is shared)
+    // The U values of stage i seed the accumulator, so the MFMAs produce U + W2^T X directly.
+    auto read_u = [&](int i) -> f32x16_t {
+        const uint8_t* p = ring + (i % RG::kNS) * RG::kStage + u_off;
+        const f32x4_t q0 = *reinterpret_cast<const f32x4_t*>(p);
+        const f32x4_t q1 = *reinterpret_cast<const f32x4_t*>(p + 16);
+        const f32x4_t q2 = *reinterpret_cast<const f32x4_t*>(p + 32);
+        const f32x4_t q3 = *reinterpret_cast<const f32x4_t*>(p + 48);
+        const f32x8_t lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8_t hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    };
+    auto frag = [&](int i, int j) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(ring + (i % RG::kNS) * RG::kStage + a_off + 32 * j);
+    };
+    // Start of a tile's epilogue (needs all 16 values): optional tail mask, tile max, running max and rescale.
+    // Returns the tile max; mc = m * c afterwards.
+    auto tile_head = [&](f32x16_t& lv, int t, auto mask_tail, float& mc) -> float {
+        if (decltype(mask_tail)::value) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t base = k2 ^ (uint32_t)(vl + 8 * q);
-                const uint32_t y = base ^ (base >> 16);
-#pragma unroll
-                for (int o = 0; o < 4; ++o) {
-                    uint32_t h = y ^ (uint32_t)o;
-                    h *= 0x85EBCA6Bu;
-                    h ^= h >> 13;
-                    h *= 0xC2B2AE35u;
-                    h ^= h >> 16;
-                    const float uu = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, h, 9)) - 0.99999994039535522f;
-                    E[4 * q + o] = -fast_log2(uu);  // -log2 u > 0
-                }
-            }
-        }
-        float lv[16];
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) lv[i2] = acc[i2] + u[i2];
-        if (v0 + kRTileV > a.V) {
-#pragma unroll
-            for (int i2 = 0; i2 < 16; ++i2)
-                if (vl + 8 * (i2 >> 2) + (i2 & 3) >= a.V) lv[i2] = -INFINITY;
+            for (int j = 0; j < 16; ++j)
+                if (t * kRTileV + 16 * half + j >= a.V) lv[j] = -INFINITY;
         }
         float cm = fmaxf(fmaxf(lv[0], lv[1]), lv[2]);
 #pragma unroll
-        for (int i2 = 3; i2 < 15; i2 += 2) cm = fmaxf(fmaxf(cm, lv[i2]), lv[i2 + 1]);
+        for (int j = 3; j < 15; j += 2) cm = fmaxf(fmaxf(cm, lv[j]), lv[j + 1]);
         cm = fmaxf(cm, lv[15]);
         const float mn = fmaxf(m, cm);
         const float scale = fast_exp2((m - mn) * c);
-        const float mc = mn * c;
         s *= scale;
+        if (SAMPLE) bp *= scale;
         m = mn;
-        float e[16];
+        mc = mn * c;
+        return cm;
+    };
+    // Greedy pick update of a tile (after its MFMA successor has been issued: it may branch).  A lane's ids
+    // ascend with the slot, so the first slot equal to the tile max is the lowest id.
+    auto greedy_pick = [&](const f32x16_t& lv, float cm, int t) {
+        if (cm > bl) {
+            int sl = 15;
 #pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) {
-            e[i2] = fast_exp2(fmaf(lv[i2], c, -mc));
-            s += e[i2];
+            for (int j = 14; j >= 0; --j) sl = (lv[j] == cm) ? j : sl;
+            bl = cm;
+            bslot = sl;
+            btile = t;
         }
+    };
+    // Per element j of the tile: exponential of the log-sum-exp and, for sampling, the noise and the race.
+    // Noise: fmix32(k2 ^ v) with v = y0 + j, y0 = 32 t + 16 half a multiple of 16, so k2 ^ v = (k2 ^ y0) ^ j
+    // and the first xor-shift of fmix32 is shared by the 16 ids: yb = kb ^ (kb >> 16), kb = k2 ^ y0.
+    auto tile_elem = [&](const f32x16_t& lv, int j, float mc, uint32_t yb, bool& improved) {
+        const float e = fast_exp2(fmaf(lv[j], c, -mc));
+        s += e;
         if (SAMPLE) {
+            uint32_t h = (yb ^ (uint32_t)j) * 0x85EBCA6Bu;
+            h ^= h >> 13;
+            h *= 0xC2B2AE35u;
+            h ^= h >> 16;
+            const float uu = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, h, 9)) - 0.99999994039535522f;
+            const float E = -fast_log2(uu);  // -log2 u > 0
             // exponential race: p / E > bp / bE  <=>  l c - log2 E beats the best so far
-            bp *= scale;
-#pragma unroll
-            for (int i2 = 0; i2 < 16; ++i2) {
-                const bool better = e[i2] * bE > bp * E[i2];
-                bp = better ? e[i2] : bp;
-                bE = better ? E[i2] : bE;
-                bi = better ? (vl + 8 * (i2 >> 2) + (i2 & 3)) : bi;
-            }
-        } else {
-#pragma unroll
-            for (int i2 = 0; i2 < 16; ++i2) {
-                const bool better = lv[i2] > bl;
-                bl = better ? lv[i2] : bl;
-                bi = better ? (vl + 8 * (i2 >> 2) + (i2 & 3)) : bi;
-            }
+            const bool better = e * bE > bp * E;
+            bp = better ? e : bp;
+            bE = better ? E : bE;
+            bslot = better ? j : bslot;
+            improved |= better;
         }
+    };
+    auto noise_base = [&](int t) -> uint32_t {
+        const uint32_t kb = k2 ^ (uint32_t)(t * kRTileV + 16 * half);
+        return kb ^ (kb >> 16);
+    };
+    // Tile tt's epilogue in one straight-line block with the operand reads and the MFMAs of tile tt + 1 (into
+    // nxt), so the matrix cores' dependent accumulation chain runs under the vector ALUs' work.
+    auto pipelined = [&](f32x16_t& cur, f32x16_t& nxt, int i, int t) {
+        const std::integral_constant<bool, false> kUnmasked{};
+        float mc;
+        const float cm = tile_head(cur, t, kUnmasked, mc);
+        const uint32_t yb = SAMPLE ? noise_base(t) : 0u;
+        nxt = read_u(i + 1);
+        bool improved = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < RK) nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i + 1, j), xf[j], nxt, 0, 0, 0);
+            tile_elem(cur, j, mc, yb, improved);
+        }
+        if (SAMPLE) btile = improved ? t : btile;
+        else greedy_pick(cur, cm, t);
+    };
+    auto last = [&](f32x16_t& cur, int t, auto mask_tail) {
+        float mc;
+        const float cm = tile_head(cur, t, mask_tail, mc);
+        const uint32_t yb = SAMPLE ? noise_base(t) : 0u;
+        bool improved = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tile_elem(cur, j, mc, yb, improved);
+        if (SAMPLE) btile = improved ? t : btile;
+        else greedy_pick(cur, cm, t);
     };
 
     const int nseg = a.K * nrb;
@@ -358,7 +401,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 if (k == 0) {
                     pv = a.anchor[b];
                 } else {
-                    const unsigned long long wv = __hip_atomic_load(a.winners + (size_t)(k - 1) * a.Bpad + b,
+                    const unsigned long long wv = __hip_atomic_load(a.winners + ((size_t)(k - 1) * a.Bpad + b) * kWinnerStride,
                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     pv = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
                     pv = min(max(pv, 0), a.V - 1);
@@ -392,35 +435,49 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         bp = 0.f;
         bE = 1.f;
         bl = -INFINITY;
-        bi = 0x7FFFFFFF;
+        bslot = 0;
+        btile = -1;
 
-        // software pipeline over the segment's tiles: the MFMAs of tile tt+1 are issued before the
-        // epilogue of tile tt, so the matrix cores work while the vector ALUs finish the previous tile
-        f32x16_t acc_cur, acc_nxt;
-        float u_cur[16], u_nxt[16];
+        // Software pipeline over the segment's tiles, unrolled by two so the accumulator sets alternate.
+        f32x16_t acc_a, acc_b;
+        const std::integral_constant<bool, true> kMasked{};
+        const std::integral_constant<bool, false> kUnmasked{};
         wait_ready(i0);
-        if (wave_live) stage_mma(i0, acc_cur, u_cur);
-        wait_lgkmcnt0();
-        if (lane == 0) lds_add(&freed[i0 % RG::kNS], 1u);
-        for (int tt = 0; tt < ntw; ++tt) {
-            const int i = i0 + tt;
-            const bool has_next = tt + 1 < ntw;
-            if (has_next) {
-                wait_ready(i + 1);
-                if (wave_live) stage_mma(i + 1, acc_nxt, u_nxt);
-            }
-            if (wave_live) epilogue(acc_cur, u_cur, t0 + tt);
-            if (has_next) {
-                wait_lgkmcnt0();
-                if (lane == 0) lds_add(&freed[(i + 1) % RG::kNS], 1u);  // the stage's bytes are in registers now
-                acc_cur = acc_nxt;
+        if (wave_live) {
+            acc_a = read_u(i0);
 #pragma unroll
-                for (int i2 = 0; i2 < 16; ++i2) u_cur[i2] = u_nxt[i2];
+            for (int j = 0; j < RK; ++j) acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i0, j), xf[j], acc_a, 0, 0, 0);
+        }
+        release(i0);
+        int tt = 0;
+        for (; tt + 2 < ntw; tt += 2) {
+            wait_ready(i0 + tt + 1);
+            if (wave_live) pipelined(acc_a, acc_b, i0 + tt, tile_of(tt));
+            release(i0 + tt + 1);
+            wait_ready(i0 + tt + 2);
+            if (wave_live) pipelined(acc_b, acc_a, i0 + tt + 1, tile_of(tt + 1));
+            release(i0 + tt + 2);
+        }
+        // one or two tiles left, the first in acc_a; only the segment's last tile can be the vocabulary's tail
+        const bool tail = tile_of(ntw - 1) == a.ntiles - 1 && a.ntiles * kRTileV > a.V;
+        if (tt + 1 < ntw) {
+            wait_ready(i0 + tt + 1);
+            if (wave_live) pipelined(acc_a, acc_b, i0 + tt, tile_of(tt));
+            release(i0 + tt + 1);
+            if (wave_live) {
+                if (tail) last(acc_b, tile_of(tt + 1), kMasked);
+                else last(acc_b, tile_of(tt + 1), kUnmasked);
+            }
+        } else if (tt < ntw) {
+            if (wave_live) {
+                if (tail) last(acc_a, tile_of(tt), kMasked);
+                else last(acc_a, tile_of(tt), kUnmasked);
             }
         }
 
         // end of this position / row block: lane merge, global pick, log-sum-exp partials
         if (wave_live) {
+            int bi = (btile >= 0) ? 32 * btile + 16 * half + bslot : 0x7FFFFFFF;
             float key, lbest;
             if (SAMPLE) {
                 const float lc = fast_log2(bp) + m * c;  // l_best * c
@@ -446,7 +503,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             if (half == 0 && valid_b) {
                 const unsigned long long packed =
                     ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
-                atomicMax(a.winners + (size_t)k * a.Bpad + b, packed);
+                atomicMax(a.winners + ((size_t)k * a.Bpad + b) * kWinnerStride, packed);
                 const size_t o = ((size_t)k * G + g) * a.Bpad + b;
                 a.p_mc[o] = mc2;
                 a.p_s[o] = s2;
@@ -468,7 +525,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
 }
 
 __global__ void round_init_kernel(unsigned long long* winners, size_t n, uint32_t* counters, uint32_t* error) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) winners[i] = 0ull;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        winners[i * kWinnerStride] = 0ull;
     if (blockIdx.x == 0 && threadIdx.x < kNumCounters) counters[kCounterStride * threadIdx.x] = 0u;
     if (blockIdx.x == 0 && threadIdx.x == 0) *error = 0u;
 }
@@ -478,7 +536,7 @@ __global__ void round_init_kernel(unsigned long long* winners, size_t n, uint32_
 __global__ void __launch_bounds__(64) round_finalize_kernel(RoundArgs a, int32_t* tokens, float* logprobs, float inv_t) {
     const int b = blockIdx.x, k = blockIdx.y, lane = threadIdx.x;
     const int G = a.G;
-    const unsigned long long wv = a.winners[(size_t)k * a.Bpad + b];
+    const unsigned long long wv = a.winners[((size_t)k * a.Bpad + b) * kWinnerStride];
     const int tok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
     float mc = kMinFinite, s = 0.f, l = 0.f;
     int found = 0;
