@@ -6,12 +6,12 @@
 // parallel, (3) walk.  Section "What the two methods do" gives the score
 // S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >.
 //
-// top-k: one workgroup per row streams the row once (16-byte loads); every thread keeps a sorted
-// register list of its best candidates, the lists are merged through LDS by repeated workgroup arg-max.
+// top-k: one workgroup per row streams the row once (independent 16-byte loads); each wave filters the
+// elements against the 16th entry of its exact running top-16 and merges the rare survivors by wave arg-max.
 // Rows with k > 16 (small vocabularies only) are sorted whole in LDS by a bitonic network.
 // Pair scores: one workgroup per (row, position, block of 16 predecessors); the 16 gated predecessor
-// rows and each block of 16 candidate rows are staged in LDS as fp32, one thread per pair.
-// Walk: one wave per row, K serial picks over the precomputed rows.
+// rows and each block of 16 candidate rows are staged in LDS as fp32 (16-byte loads), one thread per pair.
+// Walk: one wave per row, K serial picks over the precomputed rows, staged in LDS first.
 #include "internal.hpp"
 
 namespace dspark {
@@ -25,102 +25,161 @@ __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-template <int L>
-__device__ __forceinline__ void list_insert(float (&kv)[L], int (&ki)[L], float x, int v) {
-    // x beats the current last entry; put it there and bubble it up
-    kv[L - 1] = x;
-    ki[L - 1] = v;
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkUnroll = 4;  // independent 16-byte loads in flight per lane (8 waves per SIMD keep ~128 KB per CU in flight)
+constexpr int kTkBuf = 256;                  // candidate slots per wave
+constexpr int kTkSlots = kTkBuf / 64 + 1;    // merge entries per lane: its share of the buffer + one list entry
+
+// Exact top-16 of a wave's list (entry s in lane s, s < 16) and the first cnt candidates of its buffer:
+// 16 rounds of wave arg-max under (value desc, id asc).  Entries are distinct (value, id) pairs apart from
+// the empty (-inf, INT_MAX) filler, so each round removes exactly the element it emits.
+__device__ __forceinline__ void wave_top16_merge(const float* bv, const int* bi, int cnt, float& tv, int& ti) {
+    const int lane = threadIdx.x & 63;
+    float ev[kTkSlots];
+    int ei[kTkSlots];
 #pragma unroll
-    for (int s = L - 1; s > 0; --s) {
-        const bool sw = before(kv[s], ki[s], kv[s - 1], ki[s - 1]);
-        const float tv = kv[s];
-        const int ti = ki[s];
-        kv[s] = sw ? kv[s - 1] : tv;
-        ki[s] = sw ? ki[s - 1] : ti;
-        kv[s - 1] = sw ? tv : kv[s - 1];
-        ki[s - 1] = sw ? ti : ki[s - 1];
+    for (int m = 0; m < kTkSlots - 1; ++m) {
+        const int e = lane + 64 * m;
+        ev[m] = e < cnt ? bv[e] : -INFINITY;
+        ei[m] = e < cnt ? bi[e] : 0x7FFFFFFF;
     }
+    ev[kTkSlots - 1] = lane < 16 ? tv : -INFINITY;
+    ei[kTkSlots - 1] = lane < 16 ? ti : 0x7FFFFFFF;
+    float nv = -INFINITY;
+    int ni = 0x7FFFFFFF;
+    for (int out = 0; out < 16; ++out) {
+        float lv = ev[0];
+        int li = ei[0], ls = 0;
+#pragma unroll
+        for (int m = 1; m < kTkSlots; ++m)
+            if (before(ev[m], ei[m], lv, li)) {
+                lv = ev[m];
+                li = ei[m];
+                ls = m;
+            }
+        float wv = lv;
+        int wi = li;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(wv, off);
+            const int oi = __shfl_xor(wi, off);
+            if (before(ov, oi, wv, wi)) {
+                wv = ov;
+                wi = oi;
+            }
+        }
+        if (lane == out) {
+            nv = wv;
+            ni = wi;
+        }
+        if (lv == wv && li == wi) {
+#pragma unroll
+            for (int m = 0; m < kTkSlots; ++m)
+                if (m == ls) {
+                    ev[m] = -INFINITY;
+                    ei[m] = 0x7FFFFFFF;
+                }
+        }
+    }
+    tv = nv;
+    ti = ni;
 }
 
-// Top-k (k <= L) of each row.
-template <int L, bool VEC>
-__global__ void __launch_bounds__(kTkThreads) topk_kernel(const float* __restrict__ U, int64_t u_stride, int V, int k,
+// Top-k (k <= 16) of each row, one workgroup per row.  Each wave keeps an exact top-16 list (one entry per
+// lane 0..15) and its 16th entry as a threshold; every element is compared once against the threshold and
+// the few that beat it are appended to the wave's LDS buffer, which is merged into the list when it fills.
+// The row is streamed with kTkUnroll independent 16-byte loads per lane, so the scan runs at memory speed;
+// the four lists are merged at the end.
+template <bool VEC>
+__global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(8))) topk_kernel(const float* __restrict__ U, int64_t u_stride, int V, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ val) {
-    __shared__ float sk[kTkThreads * L];
-    __shared__ int si[kTkThreads * L];
-    __shared__ float wk[4];
-    __shared__ int wi[4], wt[4];
+    __shared__ float bufv[kTkWaves][kTkBuf];
+    __shared__ int bufi[kTkWaves][kTkBuf];
+    __shared__ float finv[kTkWaves * 16];
+    __shared__ int fini[kTkWaves * 16];
 
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x;
     const float* u = U + (size_t)row * u_stride;
-    float kv[L];
-    int ki[L];
-#pragma unroll
-    for (int s = 0; s < L; ++s) {
-        kv[s] = -INFINITY;
-        ki[s] = 0x7FFFFFFF;
-    }
-    // every thread scans its ids in increasing order, so an equal value seen later has a larger id
+    float* bv = bufv[wave];
+    int* bi = bufi[wave];
+    float tv = -INFINITY, thv = -INFINITY;  // this lane's list entry; the wave's threshold (list entry 15)
+    int ti = 0x7FFFFFFF, thi = 0x7FFFFFFF;
+    int cnt = 0;                            // wave-uniform buffer fill
+
+    auto flush = [&]() {
+        wave_top16_merge(bv, bi, cnt, tv, ti);
+        thv = __shfl(tv, 15);
+        thi = __shfl(ti, 15);
+        cnt = 0;
+    };
+    auto offer = [&](float x, int id) {
+        const bool p = before(x, id, thv, thi);
+        const uint64_t msk = __ballot(p);
+        if (msk) {
+            if (p) {
+                const int slot = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+                bv[slot] = x;
+                bi[slot] = id;
+            }
+            cnt += __popcll(msk);
+            if (cnt > kTkBuf - 64) flush();
+        }
+    };
     if (VEC) {
-        const int nv = V >> 2;
-        for (int q = threadIdx.x; q < nv; q += kTkThreads) {
-            const f32x4_t x = load_nt_f32x4(u + 4 * q);
-            const float xs[4] = {x.x, x.y, x.z, x.w};
+        const int nq = V >> 2;
+        const f32x4_t* u4 = reinterpret_cast<const f32x4_t*>(u);
+        for (int q0 = 0; q0 < nq; q0 += kTkThreads * kTkUnroll) {
+            f32x4_t x[kTkUnroll];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (before(xs[e], 4 * q + e, kv[L - 1], ki[L - 1])) list_insert<L>(kv, ki, xs[e], 4 * q + e);
+            for (int j = 0; j < kTkUnroll; ++j) {
+                const int q = q0 + j * kTkThreads + (int)threadIdx.x;
+                x[j] = q < nq ? __builtin_nontemporal_load(u4 + q) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            }
+#pragma unroll
+            for (int j = 0; j < kTkUnroll; ++j) {
+                const int q = q0 + j * kTkThreads + (int)threadIdx.x;
+                const int id = q < nq ? 4 * q : 0x7FFFFFFC;
+                const bool any = before(x[j].x, id, thv, thi) || before(x[j].y, id + 1, thv, thi) ||
+                                 before(x[j].z, id + 2, thv, thi) || before(x[j].w, id + 3, thv, thi);
+                if (__ballot(any)) {
+                    offer(x[j].x, id);
+                    offer(x[j].y, id + 1);
+                    offer(x[j].z, id + 2);
+                    offer(x[j].w, id + 3);
+                }
+            }
         }
     } else {
-        for (int v = threadIdx.x; v < V; v += kTkThreads) {
-            const float x = u[v];
-            if (before(x, v, kv[L - 1], ki[L - 1])) list_insert<L>(kv, ki, x, v);
+        for (int v0 = 0; v0 < V; v0 += kTkThreads * kTkUnroll) {
+            float x[kTkUnroll];
+#pragma unroll
+            for (int j = 0; j < kTkUnroll; ++j) {
+                const int v = v0 + j * kTkThreads + (int)threadIdx.x;
+                x[j] = v < V ? u[v] : -INFINITY;
+            }
+#pragma unroll
+            for (int j = 0; j < kTkUnroll; ++j) {
+                const int v = v0 + j * kTkThreads + (int)threadIdx.x;
+                offer(x[j], v < V ? v : 0x7FFFFFFF);
+            }
         }
     }
-#pragma unroll
-    for (int s = 0; s < L; ++s) {
-        sk[threadIdx.x * L + s] = kv[s];
-        si[threadIdx.x * L + s] = ki[s];
+    if (cnt > 0) flush();
+    if (lane < 16) {
+        finv[wave * 16 + lane] = tv;
+        fini[wave * 16 + lane] = ti;
     }
     __syncthreads();
-    // k rounds of workgroup arg-max over the heads of the 256 sorted lists
-    int head = 0;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int out = 0; out < k; ++out) {
-        float bk = head < L ? sk[threadIdx.x * L + head] : -INFINITY;
-        int bi = head < L ? si[threadIdx.x * L + head] : 0x7FFFFFFF;
-        int bt = threadIdx.x;
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ok_ = __shfl_xor(bk, off);
-            const int oi = __shfl_xor(bi, off);
-            const int ot = __shfl_xor(bt, off);
-            if (before(ok_, oi, bk, bi)) {
-                bk = ok_;
-                bi = oi;
-                bt = ot;
-            }
+    if (wave == 0) {
+        float fv = -INFINITY;
+        int fi = 0x7FFFFFFF;
+        wave_top16_merge(finv, fini, kTkWaves * 16, fv, fi);
+        if (lane < k) {
+            idx[(size_t)row * k + lane] = fi;
+            if (val) val[(size_t)row * k + lane] = fv;
         }
-        if (lane == 0) {
-            wk[wave] = bk;
-            wi[wave] = bi;
-            wt[wave] = bt;
-        }
-        __syncthreads();
-        float gk = wk[0];
-        int gi = wi[0], gt = wt[0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            if (before(wk[w], wi[w], gk, gi)) {
-                gk = wk[w];
-                gi = wi[w];
-                gt = wt[w];
-            }
-        }
-        if (threadIdx.x == gt) ++head;
-        if (threadIdx.x == 0) {
-            idx[(size_t)row * k + out] = gi;
-            if (val) val[(size_t)row * k + out] = gk;
-        }
-        __syncthreads();
     }
 }
 
@@ -176,10 +235,15 @@ constexpr int kPairBlock = 16;
 constexpr int kPairChunk = 256;  // rank elements staged per pass
 
 // grid: (B*K, ceil(npred / 16)); scores layout per row b: [topk] anchor row, then (K-1) tables [topk][topk].
-template <typename WT>
+// The block's predecessor and candidate rows are staged as fp32 (gated rows times H), VEC: 16-byte loads,
+// several per thread issued together.
+template <typename WT, bool VEC>
 __global__ void __launch_bounds__(256) pair_score_kernel(SelectorArgs a) {
+    constexpr int EV = 16 / (int)sizeof(WT);  // elements per 16-byte load
+    constexpr int kReps = 4;                  // loads in flight per thread
     __shared__ float ap[kPairBlock][kPairChunk + 1];
     __shared__ float bc[kPairBlock][kPairChunk + 1];
+    __shared__ int rid[2 * kPairBlock];       // predecessor rows, then candidate rows
     const WT* A = reinterpret_cast<const WT*>(a.A);
     const WT* Bm = reinterpret_cast<const WT*>(a.Bemb);
     const int bt = blockIdx.x, b = bt / a.K, t = bt % a.K;
@@ -197,39 +261,98 @@ __global__ void __launch_bounds__(256) pair_score_kernel(SelectorArgs a) {
     const int ii = threadIdx.x / kPairBlock, jj = threadIdx.x % kPairBlock;
     for (int j0 = 0; j0 < a.topk; j0 += kPairBlock) {
         const int nj = min(kPairBlock, a.topk - j0);
+        __syncthreads();
+        if ((int)threadIdx.x < ni) rid[threadIdx.x] = (t == 0) ? a.anchor[b] : cand_p[i0 + threadIdx.x];
+        if ((int)threadIdx.x >= 64 && (int)threadIdx.x < 64 + nj) rid[kPairBlock + threadIdx.x - 64] = cand_t[j0 + threadIdx.x - 64];
+        const float ub = (ii < ni && jj < nj) ? Ut[cand_t[j0 + jj]] : 0.f;
         float acc = 0.f;
         for (int q0 = 0; q0 < r; q0 += kPairChunk) {
             const int nq = min(kPairChunk, r - q0);
             __syncthreads();
-            for (int e = threadIdx.x; e < ni * nq; e += 256) {
-                const int pi = e / nq, q = e % nq;
-                const int pa = (t == 0) ? a.anchor[b] : cand_p[i0 + pi];
-                float x = wget<WT>(A, (size_t)pa * r + q0 + q);
-                if (Ht) x *= Ht[q0 + q];
-                ap[pi][q] = x;
-            }
-            for (int e = threadIdx.x; e < nj * nq; e += 256) {
-                const int cj = e / nq, q = e % nq;
-                bc[cj][q] = wget<WT>(Bm, (size_t)cand_t[j0 + cj] * r + q0 + q);
+            if (VEC) {
+                const int nvec = nq / EV;
+                const int total = (ni + nj) * nvec;
+                for (int e0 = 0; e0 < total; e0 += 256 * kReps) {
+                    u32x4_t raw[kReps];
+#pragma unroll
+                    for (int rep = 0; rep < kReps; ++rep) {
+                        const int e = e0 + rep * 256 + (int)threadIdx.x;
+                        if (e < total) {
+                            const int row = e / nvec, c = e - (e / nvec) * nvec;
+                            const WT* src = (row < ni ? A + (size_t)rid[row] * r : Bm + (size_t)rid[kPairBlock + row - ni] * r) + q0 + c * EV;
+                            raw[rep] = *reinterpret_cast<const u32x4_t*>(src);
+                        }
+                    }
+#pragma unroll
+                    for (int rep = 0; rep < kReps; ++rep) {
+                        const int e = e0 + rep * 256 + (int)threadIdx.x;
+                        if (e < total) {
+                            const int row = e / nvec, c = e - (e / nvec) * nvec;
+                            float f[EV];
+                            if (sizeof(WT) == 2) {
+                                const uint32_t w[4] = {raw[rep].x, raw[rep].y, raw[rep].z, raw[rep].w};
+#pragma unroll
+                                for (int h = 0; h < 4; ++h) {
+                                    f[2 * h] = bf16_to_f32((uint16_t)(w[h] & 0xFFFFu));
+                                    f[2 * h + 1] = bf16_to_f32((uint16_t)(w[h] >> 16));
+                                }
+                            } else {
+                                const uint32_t w[4] = {raw[rep].x, raw[rep].y, raw[rep].z, raw[rep].w};
+#pragma unroll
+                                for (int h = 0; h < EV; ++h) f[h] = __uint_as_float(w[h]);
+                            }
+                            float* dst = row < ni ? &ap[row][c * EV] : &bc[row - ni][c * EV];
+#pragma unroll
+                            for (int h = 0; h < EV; ++h) dst[h] = (row < ni && Ht) ? f[h] * Ht[q0 + c * EV + h] : f[h];
+                        }
+                    }
+                }
+            } else {
+                for (int e = threadIdx.x; e < (ni + nj) * nq; e += 256) {
+                    const int row = e / nq, q = e % nq;
+                    if (row < ni) {
+                        float x = wget<WT>(A, (size_t)rid[row] * r + q0 + q);
+                        if (Ht) x *= Ht[q0 + q];
+                        ap[row][q] = x;
+                    } else {
+                        bc[row - ni][q] = wget<WT>(Bm, (size_t)rid[kPairBlock + row - ni] * r + q0 + q);
+                    }
+                }
             }
             __syncthreads();
             if (ii < ni && jj < nj)
                 for (int q = 0; q < nq; ++q) acc = fmaf(ap[ii][q], bc[jj][q], acc);
         }
-        if (ii < ni && jj < nj) out[(size_t)(i0 + ii) * a.topk + j0 + jj] = Ut[cand_t[j0 + jj]] + acc;
+        if (ii < ni && jj < nj) out[(size_t)(i0 + ii) * a.topk + j0 + jj] = ub + acc;
     }
 }
 
-// One wave per row: K serial picks.
+// One wave per row: K serial picks.  STAGED: the row's score tables and candidate ids are first copied to
+// LDS with independent loads, so the serial chain runs on LDS latency instead of memory latency.
+template <bool STAGED>
 __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
+    extern __shared__ float wsh[];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const size_t tstride = a.topk + (size_t)(a.K - 1) * a.topk * a.topk;
     const float* sc = a.scores + (size_t)b * tstride;
+    const int32_t* cands = a.cand + (size_t)b * a.K * a.topk;
+    if (STAGED) {
+        float* ss = wsh;
+        int32_t* cs = reinterpret_cast<int32_t*>(wsh + tstride);
+        const int nc = a.K * a.topk;
+#pragma unroll 8
+        for (int i = lane; i < (int)tstride; i += 64) ss[i] = sc[i];
+#pragma unroll 4
+        for (int i = lane; i < nc; i += 64) cs[i] = cands[i];
+        __syncthreads();
+        sc = ss;
+        cands = cs;
+    }
     int islot = 0;
     for (int t = 0; t < a.K; ++t) {
         const float* rowp = (t == 0) ? sc : sc + a.topk + ((size_t)(t - 1) * a.topk + islot) * a.topk;
-        const int32_t* cand_t = a.cand + ((size_t)b * a.K + t) * a.topk;
+        const int32_t* cand_t = cands + (size_t)t * a.topk;
         const uint32_t k2 = a.sample ? noise_key2(a.k0, (uint32_t)b, (uint32_t)t) : 0u;
         float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
         int bi = 0x7FFFFFFF, bs = 0;
@@ -246,7 +369,9 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
             }
             lse_merge(m, s, tt, 1.0f);
         }
-        for (int off = 32; off > 0; off >>= 1) {
+        // reduce over the lanes that hold candidates (a 16-lane group when topk <= 16)
+        const int span = a.topk <= 16 ? 16 : 64;
+        for (int off = span >> 1; off > 0; off >>= 1) {
             const float ok_ = __shfl_xor(bk, off);
             const int oi = __shfl_xor(bi, off);
             const float ol = __shfl_xor(bl, off);
@@ -277,8 +402,8 @@ hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int to
                        hipStream_t st) {
     const bool vec = (V % 4 == 0) && (u_stride % 4 == 0) && ((uintptr_t)U % 16 == 0);
     if (topk <= 16) {
-        if (vec) hipLaunchKernelGGL((topk_kernel<16, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
-        else hipLaunchKernelGGL((topk_kernel<16, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        if (vec) hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        else hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
     } else if (V <= kSortMax) {
         hipLaunchKernelGGL(topk_sort_kernel, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
     } else {
@@ -291,13 +416,21 @@ int topk_supported(int V, int topk) { return topk >= 1 && topk <= V && (topk <= 
 
 hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
     const dim3 grid(a.B * a.K, (a.topk + kPairBlock - 1) / kPairBlock);
-    if (a.bf16) hipLaunchKernelGGL(pair_score_kernel<uint16_t>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(pair_score_kernel<float>, grid, dim3(256), 0, st, a);
+    const bool vec = ((uintptr_t)a.A % 16 == 0) && ((uintptr_t)a.Bemb % 16 == 0) && (a.r % (a.bf16 ? 8 : 4) == 0);
+    if (a.bf16) {
+        if (vec) hipLaunchKernelGGL((pair_score_kernel<uint16_t, true>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((pair_score_kernel<uint16_t, false>), grid, dim3(256), 0, st, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((pair_score_kernel<float, true>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((pair_score_kernel<float, false>), grid, dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_walk(const SelectorArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(walk_kernel, dim3(a.B), dim3(64), 0, st, a);
+    const size_t lds = sizeof(float) * (a.topk + (size_t)(a.K - 1) * a.topk * a.topk + (size_t)a.K * a.topk);
+    if (lds <= 64 * 1024) hipLaunchKernelGGL(walk_kernel<true>, dim3(a.B), dim3(64), lds, st, a);
+    else hipLaunchKernelGGL(walk_kernel<false>, dim3(a.B), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 
