@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "calibrated draft tokens/s at B=128,K=16,V=151936,r=256; % of HBM roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "markov_step_serving_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "rank_markov_draft_amd", "csrc", "markov.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "markov_round_serving_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rank_markov_draft_amd", "csrc", "markov_round.hip")
 
 
 def markov_bytes_per_position(B, V, r, gated=False):
@@ -61,6 +61,39 @@ def traffic_entry():
     return t
 
 
+def write_traffic(fetch_csv, write_csv):
+    """Counter-measured bytes per launch of the round kernel, from two rocprofv3 --pmc passes (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) over `bench.py --no-extras --copy-calibration`.  Each counter is scaled by
+    what it reads for the 1 GiB device copy in the same run (1 GiB read, 1 GiB written)."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return out
+
+    gib_kib = float(1 << 20)
+    rec = {"kernel": "markov_round_kernel<16, sample> (serving workload)", "kernel_source_sha256_16": source_hash()}
+    total = 0.0
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        d = per_kernel(path, counter)
+        copy = max(d["__amd_rocclr_copyBuffer"])
+        kern = [v for k, v in d.items() if "markov_round_kernel<16, 1, false>" in k][0]
+        mean = sum(kern) / len(kern)
+        scale = gib_kib / copy
+        rec[key] = {"counter": counter, "kib_per_launch": round(mean, 1), "launches": len(kern),
+                    "copy_kib_for_1gib": round(copy, 1), "scale": round(scale, 5),
+                    "bytes_per_launch": int(round(mean * 1024 * scale))}
+        total += mean * 1024 * scale
+    rec["bytes_per_launch"] = int(round(total))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,7 +104,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference kernel for the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the counter-measured traffic record from two rocprofv3 --pmc counter_collection.csv "
+                         "files and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
