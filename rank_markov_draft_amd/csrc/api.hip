@@ -1,4 +1,6 @@
 // api.hip -- the extern "C" boundary of libdspark: argument checks, workspace carving, dispatch.
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -53,7 +55,17 @@ int round_gmax() {
     return n < kMaxG ? n : kMaxG;
 }
 
-constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines) and the error word
+constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines), the error word, the init flag
+
+// Sequence numbers of whole-round launches: the kernel clears its own counters and marks the clearing with
+// the call's number, so a stale flag left in a reused workspace by an earlier call never matches.  The
+// start is drawn from the clock so that two processes sharing memory are unlikely to collide.
+uint64_t next_call_seq() {
+    static std::atomic<uint64_t> seq{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
+    uint64_t s;
+    do s = seq.fetch_add(1, std::memory_order_relaxed) + 1; while (s == 0);
+    return s;
+}
 
 // winners [K][Bpad] u64 (kWinnerStride words apart), the counters, four [K][Gmax][Bpad] partial arrays
 size_t round_region_bytes(int B, int K) {
@@ -264,13 +276,17 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.winners = ws.winners;
             a.barrier = ws.counters;
             a.error = ws.counters + 256;  // after the 8 counter lines (32 words apart)
+            a.flag = reinterpret_cast<uint64_t*>(ws.counters + 288);
+            a.seq = next_call_seq();
+            a.tokens = tokens;
+            a.logprobs = logprobs;
+            a.inv_t = 1.0f / teff;
             a.spin_limit = 1u << 22;
             a.p_mc = ws.p_mc;
             a.p_s = ws.p_s;
             a.p_idx = ws.p_idx;
             a.p_l = ws.p_l;
-            hipError_t e = launch_markov_round(a, sample, H != nullptr, tokens, logprobs, 1.0f / teff, st,
-                                               ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+            hipError_t e = launch_markov_round(a, sample, H != nullptr, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
             if (e != hipSuccess) return device_fail(e, "draft round launch");
             if (kernel_launches) *kernel_launches = 1;
             return DSPARK_OK;

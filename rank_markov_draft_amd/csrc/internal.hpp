@@ -76,6 +76,11 @@ struct RoundArgs {
     uint32_t* barrier;          // grid barrier counter
     uint32_t* error;            // set if a barrier wait timed out
     uint32_t spin_limit;
+    uint64_t* flag;             // set to seq by workgroup 0 once it has cleared winners, counters and error
+    uint64_t seq;               // per-call sequence number (never 0)
+    int32_t* tokens;            // [B, K] outputs, written by the kernel's finalizer waves
+    float* logprobs;            // [B, K] or null
+    float inv_t;
     float* p_mc;                // [K][G][Bpad] log-sum-exp partials (base-2 max of l c, sum)
     float* p_s;
     int* p_idx;                 // [K][G][Bpad] best id and its logit per workgroup
@@ -87,8 +92,8 @@ constexpr int kWinnerStride = 16;
 int round_supported_r(int r);
 int round_lds_bytes(int r);
 int round_max_coresident(int r, bool sample, bool gated);
-hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, int32_t* tokens, float* logprobs,
-                               float inv_t, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
+                               hipEvent_t ev_end);
 
 int mfma_supported_r(int r);
 hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);

@@ -26,7 +26,9 @@
 //  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id) gives the global
 //    pick with ties to the lower id; log-sum-exp partials go to the workspace.  A grid barrier (counter,
 //    bounded spin) then releases the next position, whose workgroups gather W1 rows of the new tokens.
-//  * A finalize kernel merges the log-sum-exp partials of all positions into tokens and log-probabilities.
+//  * A ninth wave per workgroup (the finalizer) clears the pick words and counters at the start of the launch
+//    and, one position behind, merges the log-sum-exp partials of its rows into tokens and log-probabilities,
+//    so a round is a single launch.
 #include <type_traits>
 
 #include "common.hpp"
@@ -62,7 +64,8 @@ __device__ __forceinline__ int w2_slot(int rho) { return 8 * ((rho & 15) >> 2) +
 constexpr int kGateItems = 4;  // items of the next position that may be in flight at a position boundary
 constexpr int kConsumers = 4;
 constexpr int kProducers = 4;
-constexpr int kRoundThreads = 64 * (kConsumers + kProducers);
+constexpr int kFinalizers = 1;
+constexpr int kRoundThreads = 64 * (kConsumers + kProducers + kFinalizers);
 
 // vmcnt waits with compile-time counts (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
 template <int N>
@@ -88,6 +91,57 @@ __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
 
 constexpr int kNumCounters = 8;  // the grid barrier counter is spread over 8 cache lines
 constexpr int kCounterStride = 32;
+
+template <typename T>
+__device__ __forceinline__ T agent_load(const T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void agent_store(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t grid_arrivals(const RoundArgs& a) {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int cc = 0; cc < kNumCounters; ++cc) tot += agent_load(a.barrier + kCounterStride * cc);
+    return tot;
+}
+
+// One wave merges the G partials of (row b, position k): the pick from the winner word, the log-sum-exp over
+// the partials, the logit of the pick from the partial of the workgroup that owns its id.
+__device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) {
+    const int lane = threadIdx.x & 63;
+    const int G = a.G;
+    const unsigned long long wv = agent_load(a.winners + ((size_t)k * a.Bpad + b) * kWinnerStride);
+    const int tok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
+    float mc = kMinFinite, s = 0.f, l = 0.f;
+    int found = 0;
+    for (int gg = lane; gg < G; gg += 64) {
+        const size_t o = ((size_t)k * G + gg) * a.Bpad + b;
+        lse_merge(mc, s, agent_load(a.p_mc + o), agent_load(a.p_s + o));
+        if (agent_load(a.p_idx + o) == tok) {
+            l = agent_load(a.p_l + o);
+            found = 1;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const float omc = __shfl_xor(mc, off);
+        const float os = __shfl_xor(s, off);
+        const float ol = __shfl_xor(l, off);
+        const int of = __shfl_xor(found, off);
+        lse_merge(mc, s, omc, os);
+        if (of && !found) {
+            l = ol;
+            found = 1;
+        }
+    }
+    if (lane == 0) {
+        const bool bad = timed_out || agent_load(a.error) != 0u || !found;
+        a.tokens[(size_t)b * a.K + k] = bad ? -1 : tok;
+        if (a.logprobs) a.logprobs[(size_t)b * a.K + k] = bad ? NAN : l * a.inv_t - (mc + fast_log2(s)) * kLn2;
+    }
+}
 
 template <int RK, int MODE, bool GATED>
 __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArgs a) {
@@ -125,6 +179,48 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     }
     __syncthreads();
 
+    if (wave >= kConsumers + kProducers) {
+        // ============================================================== finalizer
+        // Workgroup 0 first clears the winner words, the grid counters and the error word, then publishes the
+        // call's sequence number; consumers check it before their first atomics.  No other launch is needed.
+        if (g == 0) {
+            const size_t nw = (size_t)a.K * a.Bpad;
+            for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i * kWinnerStride, 0ull);
+            if (lane < kNumCounters) agent_store(a.barrier + kCounterStride * lane, 0u);
+            if (lane == 0) agent_store(a.error, 0u);
+            wait_vmcnt<0>();
+            if (lane == 0) agent_store(a.flag, a.seq);
+        }
+        // Then, position by position, once every workgroup has finished it (this workgroup's release of the
+        // next position, or the grid counters after the last one): tokens and log-probabilities of rows
+        // g, g + G, ...  Until the last position this runs while the rest of the workgroup streams and
+        // computes, off the serial path.
+        for (int k = 0; k < a.K; ++k) {
+            bool timed_out = false;
+            uint32_t spins = 0;
+            if (k + 1 < a.K) {
+                while (lds_load(&released) < (uint32_t)(k + 1)) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > spin_limit) {
+                        timed_out = true;
+                        break;
+                    }
+                }
+            } else {
+                const uint32_t target = (uint32_t)G * (uint32_t)a.K;
+                while (grid_arrivals(a) < target) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > spin_limit) {
+                        timed_out = true;
+                        break;
+                    }
+                }
+            }
+            if (timed_out && lane == 0) agent_store(a.error, 1u);
+            for (int b = g; b < a.B; b += G) finalize_pair(a, b, k, timed_out);
+        }
+        return;
+    }
     if (wave >= kConsumers) {
         // ============================================================== producers: stream W2 and U tiles
         // Ordinary 16-byte vector loads into registers, kDepth items ahead, then ds_write into the padded
@@ -372,11 +468,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 const uint32_t target = (uint32_t)G * (uint32_t)k;
                 uint32_t spins = 0;
                 while (true) {
-                    uint32_t tot = 0;
-#pragma unroll
-                    for (int cc = 0; cc < kNumCounters; ++cc)
-                        tot += __hip_atomic_load(a.barrier + kCounterStride * cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (tot >= target) break;
+                    if (grid_arrivals(a) >= target) break;
                     __builtin_amdgcn_s_sleep(1);
                     if (++spins > spin_limit) {
                         __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -500,15 +592,27 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 lbest = ol;
             }
             lse_merge(mc2, s2, omc, os);
+            if (seg == 0 && lane == 0) {
+                // the winner words and counters of this call are cleared before the first atomics touch them
+                uint32_t spins = 0;
+                while (agent_load(a.flag) != a.seq) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > spin_limit) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
             if (half == 0 && valid_b) {
                 const unsigned long long packed =
                     ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
                 atomicMax(a.winners + ((size_t)k * a.Bpad + b) * kWinnerStride, packed);
                 const size_t o = ((size_t)k * G + g) * a.Bpad + b;
-                a.p_mc[o] = mc2;
-                a.p_s[o] = s2;
-                a.p_idx[o] = bi;
-                a.p_l[o] = lbest;
+                // read by other workgroups' finalizers within this launch
+                agent_store(a.p_mc + o, mc2);
+                agent_store(a.p_s + o, s2);
+                agent_store(a.p_idx + o, bi);
+                agent_store(a.p_l + o, lbest);
             }
         }
         if (rb == nrb - 1) {
@@ -521,48 +625,6 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                                            __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-    }
-}
-
-__global__ void round_init_kernel(unsigned long long* winners, size_t n, uint32_t* counters, uint32_t* error) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        winners[i * kWinnerStride] = 0ull;
-    if (blockIdx.x == 0 && threadIdx.x < kNumCounters) counters[kCounterStride * threadIdx.x] = 0u;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *error = 0u;
-}
-
-// One wave per (b, k): pick from the winner word, log-sum-exp over the G partials, logit of the pick from the
-// partial of the workgroup that owns its id.
-__global__ void __launch_bounds__(64) round_finalize_kernel(RoundArgs a, int32_t* tokens, float* logprobs, float inv_t) {
-    const int b = blockIdx.x, k = blockIdx.y, lane = threadIdx.x;
-    const int G = a.G;
-    const unsigned long long wv = a.winners[((size_t)k * a.Bpad + b) * kWinnerStride];
-    const int tok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
-    float mc = kMinFinite, s = 0.f, l = 0.f;
-    int found = 0;
-    for (int gg = lane; gg < G; gg += 64) {
-        const size_t o = ((size_t)k * G + gg) * a.Bpad + b;
-        lse_merge(mc, s, a.p_mc[o], a.p_s[o]);
-        if (a.p_idx[o] == tok) {
-            l = a.p_l[o];
-            found = 1;
-        }
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-        const float omc = __shfl_xor(mc, off);
-        const float os = __shfl_xor(s, off);
-        const float ol = __shfl_xor(l, off);
-        const int of = __shfl_xor(found, off);
-        lse_merge(mc, s, omc, os);
-        if (of && !found) {
-            l = ol;
-            found = 1;
-        }
-    }
-    if (lane == 0) {
-        const bool bad = *a.error != 0u || !found;
-        tokens[(size_t)b * a.K + k] = bad ? -1 : tok;
-        if (logprobs) logprobs[(size_t)b * a.K + k] = bad ? NAN : l * inv_t - (mc + fast_log2(s)) * kLn2;
     }
 }
 
@@ -621,13 +683,10 @@ int round_max_coresident(int r, bool sample, bool gated) {
     return per_cu * device_cu_count();
 }
 
-hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, int32_t* tokens, float* logprobs,
-                               float inv_t, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
-    const size_t nw = (size_t)a.K * a.Bpad;
-    hipLaunchKernelGGL(round_init_kernel, dim3(64), dim3(256), 0, st, a.winners, nw, a.barrier, a.error);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
+                               hipEvent_t ev_end) {
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
+    hipError_t e;
     switch (a.r / 16) {
         case 1: e = launch_round_rk<1>(a, sample, gated, st); break;
         case 2: e = launch_round_rk<2>(a, sample, gated, st); break;
@@ -637,9 +696,7 @@ hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, int3
         default: return hipErrorInvalidValue;
     }
     if (ev_end) (void)hipEventRecord(ev_end, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(round_finalize_kernel, dim3(a.B, a.K), dim3(64), 0, st, a, tokens, logprobs, inv_t);
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace dspark
