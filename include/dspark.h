@@ -164,7 +164,7 @@ int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, v
  * guide, "Markov Head": the gated variant gates the bias by the backbone hidden state).  The pages give
  * no formula; this library takes a bias-free linear map followed by the logistic sigmoid.
  * h [rows, D] bf16, Wg [D, r] bf16, H [rows, r] fp32 output.  fp32 accumulation.
- * D % 32 == 0 and r % 32 == 0 are required (DSPARK_EUNSUPPORTED otherwise).
+ * D % 256 == 0 and r % 32 == 0 are required (DSPARK_EUNSUPPORTED otherwise).
  */
 int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* stream);
 
@@ -180,7 +180,8 @@ size_t dspark_topk_workspace_bytes(int rows, int V, int topk);
  * equal.  (Equivalence page, section "Where the parallelism comes from": the candidate set of a
  * position is the top tokens under the base logits.)
  * U [rows, V] fp32 with row i at U + i * u_stride.  idx [rows, topk] int32 output, val [rows, topk]
- * fp32 output or NULL.  1 <= topk <= min(V, 64).
+ * fp32 output or NULL.  1 <= topk <= V; topk <= 64 at any V (DSPARK_EUNSUPPORTED for topk > 64 unless
+ * V <= 4096, where the row is sorted whole).
  */
 int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val,
                 void* workspace, size_t workspace_bytes, void* stream);
@@ -198,7 +199,8 @@ size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk);
  *     The pick is the same GREEDY / SAMPLE rule as the Markov head over the k candidates, keyed on
  *     vocabulary ids; logprobs[b, t] = log softmax over the walked row of scores / T.
  * U [B, K, V] fp32; A, Bemb [V, r] of type wdtype; anchor [B]; H [B, K, r] fp32 or NULL.
- * topk 1 .. min(V, 64); r % 8 == 0 and r <= 1024 for bf16 (r % 4 == 0 for fp32).
+ * topk as for dspark_topk; r <= 1024 (rows are staged with 16-byte loads when r % 8 == 0 for bf16 or
+ * r % 4 == 0 for fp32 and A, Bemb are 16-byte aligned, element by element otherwise).
  * tokens [B, K] int32 output; logprobs [B, K] fp32 or NULL; cand [B, K, topk] int32 or NULL;
  * scores [B, topk + (K-1) * topk * topk] fp32 or NULL (anchor row, then the K-1 tables, row-major i, j).
  */

@@ -7,8 +7,8 @@
 // S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >.
 //
 // top-k: one workgroup per row streams the row once (independent 16-byte loads); each wave filters the
-// elements against the 16th entry of its exact running top-16 and merges the rare survivors by wave arg-max.
-// Rows with k > 16 (small vocabularies only) are sorted whole in LDS by a bitonic network.
+// elements against the last entry of its exact running top-16 (or top-64) and merges the rare survivors by
+// wave arg-max.  Rows with k > 64 (small vocabularies only) are sorted whole in LDS by a bitonic network.
 // Pair scores: one workgroup per (row, position, block of 16 predecessors); the 16 gated predecessor
 // rows and each block of 16 candidate rows are staged in LDS as fp32 (16-byte loads), one thread per pair.
 // Walk: one wave per row, K serial picks over the precomputed rows, staged in LDS first.
@@ -30,10 +30,11 @@ constexpr int kTkUnroll = 4;  // independent 16-byte loads in flight per lane (8
 constexpr int kTkBuf = 256;                  // candidate slots per wave
 constexpr int kTkSlots = kTkBuf / 64 + 1;    // merge entries per lane: its share of the buffer + one list entry
 
-// Exact top-16 of a wave's list (entry s in lane s, s < 16) and the first cnt candidates of its buffer:
-// 16 rounds of wave arg-max under (value desc, id asc).  Entries are distinct (value, id) pairs apart from
-// the empty (-inf, INT_MAX) filler, so each round removes exactly the element it emits.
-__device__ __forceinline__ void wave_top16_merge(const float* bv, const int* bi, int cnt, float& tv, int& ti) {
+// Exact top-L (L = 16 or 64) of a wave's list (entry s in lane s, s < L) and the first cnt candidates of its
+// buffer: L rounds of wave arg-max under (value desc, id asc).  Entries are distinct (value, id) pairs apart
+// from the empty (-inf, INT_MAX) filler, so each round removes exactly the element it emits.
+template <int L>
+__device__ __forceinline__ void wave_top_merge(const float* bv, const int* bi, int cnt, float& tv, int& ti) {
     const int lane = threadIdx.x & 63;
     float ev[kTkSlots];
     int ei[kTkSlots];
@@ -43,11 +44,11 @@ __device__ __forceinline__ void wave_top16_merge(const float* bv, const int* bi,
         ev[m] = e < cnt ? bv[e] : -INFINITY;
         ei[m] = e < cnt ? bi[e] : 0x7FFFFFFF;
     }
-    ev[kTkSlots - 1] = lane < 16 ? tv : -INFINITY;
-    ei[kTkSlots - 1] = lane < 16 ? ti : 0x7FFFFFFF;
+    ev[kTkSlots - 1] = lane < L ? tv : -INFINITY;
+    ei[kTkSlots - 1] = lane < L ? ti : 0x7FFFFFFF;
     float nv = -INFINITY;
     int ni = 0x7FFFFFFF;
-    for (int out = 0; out < 16; ++out) {
+    for (int out = 0; out < L; ++out) {
         float lv = ev[0];
         int li = ei[0], ls = 0;
 #pragma unroll
@@ -85,32 +86,32 @@ __device__ __forceinline__ void wave_top16_merge(const float* bv, const int* bi,
     ti = ni;
 }
 
-// Top-k (k <= 16) of each row, one workgroup per row.  Each wave keeps an exact top-16 list (one entry per
-// lane 0..15) and its 16th entry as a threshold; every element is compared once against the threshold and
-// the few that beat it are appended to the wave's LDS buffer, which is merged into the list when it fills.
-// The row is streamed with kTkUnroll independent 16-byte loads per lane, so the scan runs at memory speed;
-// the four lists are merged at the end.
-template <bool VEC>
+// Top-k (k <= L, L = 16 or 64) of each row, one workgroup per row.  Each wave keeps an exact top-L list (one
+// entry per lane 0..L-1) and its L-th entry as a threshold; every element is compared once against the
+// threshold and the few that beat it are appended to the wave's LDS buffer, which is merged into the list
+// when it fills.  The row is streamed with kTkUnroll independent 16-byte loads per lane, so the scan runs at
+// memory speed; the four lists are merged at the end.
+template <int L, bool VEC>
 __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(8))) topk_kernel(const float* __restrict__ U, int64_t u_stride, int V, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ val) {
     __shared__ float bufv[kTkWaves][kTkBuf];
     __shared__ int bufi[kTkWaves][kTkBuf];
-    __shared__ float finv[kTkWaves * 16];
-    __shared__ int fini[kTkWaves * 16];
+    __shared__ float finv[kTkWaves * L];
+    __shared__ int fini[kTkWaves * L];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x;
     const float* u = U + (size_t)row * u_stride;
     float* bv = bufv[wave];
     int* bi = bufi[wave];
-    float tv = -INFINITY, thv = -INFINITY;  // this lane's list entry; the wave's threshold (list entry 15)
+    float tv = -INFINITY, thv = -INFINITY;  // this lane's list entry; the wave's threshold (list entry L-1)
     int ti = 0x7FFFFFFF, thi = 0x7FFFFFFF;
     int cnt = 0;                            // wave-uniform buffer fill
 
     auto flush = [&]() {
-        wave_top16_merge(bv, bi, cnt, tv, ti);
-        thv = __shfl(tv, 15);
-        thi = __shfl(ti, 15);
+        wave_top_merge<L>(bv, bi, cnt, tv, ti);
+        thv = __shfl(tv, L - 1);
+        thi = __shfl(ti, L - 1);
         cnt = 0;
     };
     auto offer = [&](float x, int id) {
@@ -167,15 +168,16 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
         }
     }
     if (cnt > 0) flush();
-    if (lane < 16) {
-        finv[wave * 16 + lane] = tv;
-        fini[wave * 16 + lane] = ti;
+    if (lane < L) {
+        finv[wave * L + lane] = tv;
+        fini[wave * L + lane] = ti;
     }
     __syncthreads();
     if (wave == 0) {
+        // the four lists (4 L entries) are merged as buffer entries into an empty list
         float fv = -INFINITY;
         int fi = 0x7FFFFFFF;
-        wave_top16_merge(finv, fini, kTkWaves * 16, fv, fi);
+        wave_top_merge<L>(finv, fini, kTkWaves * L, fv, fi);
         if (lane < k) {
             idx[(size_t)row * k + lane] = fi;
             if (val) val[(size_t)row * k + lane] = fv;
@@ -402,8 +404,11 @@ hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int to
                        hipStream_t st) {
     const bool vec = (V % 4 == 0) && (u_stride % 4 == 0) && ((uintptr_t)U % 16 == 0);
     if (topk <= 16) {
-        if (vec) hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
-        else hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        if (vec) hipLaunchKernelGGL((topk_kernel<16, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        else hipLaunchKernelGGL((topk_kernel<16, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+    } else if (topk <= 64) {
+        if (vec) hipLaunchKernelGGL((topk_kernel<64, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        else hipLaunchKernelGGL((topk_kernel<64, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
     } else if (V <= kSortMax) {
         hipLaunchKernelGGL(topk_sort_kernel, dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
     } else {
@@ -412,7 +417,7 @@ hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int to
     return hipGetLastError();
 }
 
-int topk_supported(int V, int topk) { return topk >= 1 && topk <= V && (topk <= 16 || V <= kSortMax); }
+int topk_supported(int V, int topk) { return topk >= 1 && topk <= V && (topk <= 64 || V <= kSortMax); }
 
 hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
     const dim3 grid(a.B * a.K, (a.topk + kPairBlock - 1) / kPairBlock);

@@ -27,7 +27,7 @@ def _tie_rows(rows, V, seed=0):
 
 
 @pytest.mark.parametrize("V", [16, 100, 1001, 4096, 151936])
-@pytest.mark.parametrize("k", [1, 5, 16])
+@pytest.mark.parametrize("k", [1, 5, 16, 17, 40, 64])
 def test_topk_exact(D, V, k):
     if k > V:
         pytest.skip("k > V")
@@ -49,7 +49,8 @@ def test_topk_large_k_small_vocab(D, V, k):
 
 
 SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 96, 16, 16, S.F32),
-              (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16)]
+              (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16), (3, 3, 2000, 32, 32, S.BF16),
+              (2, 3, 5000, 64, 64, S.BF16)]
 
 
 @pytest.mark.parametrize("shape", SEL_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d-k%d" % s[:5])
