@@ -255,6 +255,35 @@ def main():
                                     "tokens_per_s": round(w.B * w.K / (sms_.mean() / 1e3), 1),
                                     "bytes_per_round": sb,
                                     "pct_of_hbm_roofline": round(100.0 * sb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(sms_.mean()), 2)}
+
+        # top-k sweep: the Selector execution of the Markov rule (W1 = A, W2 = Bemb^T) restricted to the
+        # top-k candidates, against the full-vocabulary greedy head on the same inputs: token agreement and
+        # round time, on these inputs and on a strong-bias variant of them
+        sweep = {}
+        for label, wk in (("synthetic", w), ("strong_bias", S.strong("selector"))):
+            if label != "synthetic":
+                del U, A, Bemb
+                torch.cuda.empty_cache()
+                U = torch.from_numpy(wk.U).to(dev)
+                A, Bemb = to_w(wk.W1), to_w(wk.W2T)
+                anc = torch.from_numpy(wk.anchor).to(dev)
+            full, _ = D.dspark_markov_draft(U, A, Bemb, anc, w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_GREEDY)
+            fh = full.cpu().numpy()
+            row = {}
+            for kk in (4, 8, 16, 32, 64):
+                kws = torch.empty(D.dspark_selector_workspace_bytes(wk.B, wk.K, wk.V, wk.r, kk), dtype=torch.uint8,
+                                  device=dev)
+                res = D.dspark_selector_draft(U, A, Bemb, anc, topk=kk, workspace=kws)
+                th = res["tokens"].cpu().numpy()
+                same = th == fh
+                prefix = np.where(same.all(axis=1), wk.K, np.argmin(same, axis=1))
+                ent = {"agreement": round(float(same.mean()), 4), "mean_agreeing_prefix": round(float(prefix.mean()), 3)}
+                if label == "synthetic":
+                    kms, _ = timed_rounds(lambda: D.dspark_selector_draft(U, A, Bemb, anc, topk=kk, workspace=kws), 5)
+                    ent["round_ms"] = round(float(kms.mean()), 4)
+                row["k%d" % kk] = ent
+            sweep[label] = row
+        extras["topk_sweep"] = sweep
         del U, A, Bemb
         torch.cuda.empty_cache()
 

@@ -42,6 +42,7 @@ def _load():
         lib.oracle_gumbel.restype = dbl
         lib.oracle_noise_fill.argtypes = [u64, u32, u32, u32, i64, vp, vp]
         lib.oracle_gate.argtypes = [vp, vp, i32, i32, i32, vp]
+        lib.oracle_confidence.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, i32, i32, vp, vp]
         lib.oracle_markov_draft.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, dbl,
                                             vp, vp, i32, vp, vp, vp, vp, vp]
         lib.oracle_markov_logits.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp]
@@ -123,6 +124,27 @@ def gate(h: np.ndarray, Wg: np.ndarray) -> np.ndarray:
     H = np.empty(h.shape[:-1] + (r,), dtype=np.float64)
     _load().oracle_gate(_ptr(h), _ptr(Wg), rows, D, r, _ptr(H))
     return H
+
+
+# ---------------------------------------------------------------------------------------- confidence
+
+def confidence(h, w, W1, anchor, tokens):
+    """c_k = sigmoid(w_h . h_k + w_m . W1[x_{k-1}]) and the prefix survival a_k = prod_{i<=k} c_i, fp64.
+    h [B, K, D] bf16 bits; w [D + r] float32 (h part, then W1 part); W1 [V, r] float32 or bf16 bits;
+    anchor [B]; tokens [B, K] (x_{-1} is the anchor).  Returns (conf, survival), each [B, K] float64."""
+    h = _c(h, np.uint16)
+    B, K, D = h.shape
+    W1, wd = _w(W1)
+    r = W1.shape[1]
+    w = _c(w, np.float32)
+    assert w.shape == (D + r,)
+    anchor = _c(anchor, np.int32)
+    tokens = _c(tokens, np.int32)
+    conf = np.empty((B, K), np.float64)
+    surv = np.empty((B, K), np.float64)
+    _load().oracle_confidence(_ptr(h), D, _ptr(w), _ptr(W1), wd, r, _ptr(anchor), _ptr(tokens), B, K, _ptr(conf),
+                              _ptr(surv))
+    return conf, surv
 
 
 # -------------------------------------------------------------------------------------------- markov

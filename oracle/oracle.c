@@ -137,6 +137,32 @@ void oracle_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, 
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* confidence head and prefix survival                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [DSp] "Confidence-scheduled verification": c_k = sigmoid(w^T [h_k ; W1[x_{k-1}]]) is the probability that
+ * position k is accepted given that the prefix so far survived, and the prefix survival is the product
+ * a_j = prod_{i <= j} c_i.  x_{k-1} is the token drafted at position k-1; at k = 0 it is the anchor (the
+ * predecessor the Markov step uses at that position).  h [B, K, D] bf16; w [D + r] fp32, the h part first,
+ * then the W1 part; W1 [V, r] of type wdtype; tokens [B, K].  conf and survival [B, K]. */
+void oracle_confidence(const uint16_t* h, int D, const float* w, const void* W1, int wdtype, int r,
+                       const int32_t* anchor, const int32_t* tokens, int B, int K, double* conf, double* survival) {
+    for (int b = 0; b < B; ++b) {
+        double a = 1.0;
+        for (int k = 0; k < K; ++k) {
+            const int prev = (k == 0) ? anchor[b] : tokens[(size_t)b * K + k - 1];
+            double z = 0.0;
+            for (int d = 0; d < D; ++d) z += (double)w[d] * weight_at(h, OR_BF16, ((size_t)b * K + k) * D + d);
+            for (int j = 0; j < r; ++j) z += (double)w[D + j] * weight_at(W1, wdtype, (size_t)prev * r + j);
+            const double c = 1.0 / (1.0 + exp(-z));
+            a *= c;
+            conf[(size_t)b * K + k] = c;
+            survival[(size_t)b * K + k] = a;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* one calibrated position                                                                      */
 /* ------------------------------------------------------------------------------------------ */
 

@@ -376,6 +376,31 @@ def test_selector_with_topk_V_is_the_full_head(mode):
     np.testing.assert_allclose(sel["logprobs"], full["logprobs"], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("k", [2, 4, 8, 16])
+def test_truncated_greedy_is_exact_until_the_full_pick_leaves_the_candidates(k):
+    """[MvS] "Two implications", second point: an already trained head executed on the top-k candidates.
+    An argmax over a subset that contains the global argmax is the global argmax, so along every row the
+    truncated greedy walk equals the full-vocabulary greedy head up to the first position whose full pick
+    is not a candidate (fp64: no ties).  Strong bias so that the truncation does change some drafts."""
+    rng = np.random.default_rng(30 + k)
+    B, K, V, r = 12, 6, 200, 16
+    U = rng.standard_normal((B, K, V)).astype(np.float32)
+    A = S.f32_to_bf16((rng.standard_normal((V, r)) * 0.7).astype(np.float32))
+    Bemb = S.f32_to_bf16((rng.standard_normal((V, r)) * 0.7).astype(np.float32))
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    sel = O.selector_draft(U, A, Bemb, anchor, topk=k)
+    full = O.markov_draft(U, A, Bemb, anchor, w2_layout=O.W2_VR)
+    diverged = 0
+    for b in range(B):
+        d = np.nonzero(sel["tokens"][b] != full["tokens"][b])[0]
+        if d.size:
+            t = int(d[0])
+            assert full["tokens"][b, t] not in sel["cand"][b, t]
+            diverged += 1
+    if k == 2:
+        assert diverged > 0  # the inputs do exercise the truncation
+
+
 def test_selector_tables_match_numpy():
     rng = np.random.default_rng(13)
     B, K, V, r, topk = 2, 4, 30, 8, 5
@@ -423,3 +448,59 @@ def test_shift_invariance():
         assert ok.mean() > 0.9
         assert np.array_equal(a["tokens"][ok], b["tokens"][ok])
         np.testing.assert_allclose(a["logprobs"], b["logprobs"], rtol=0, atol=1e-3)
+
+
+# -------------------------------------------------------------------------------------- confidence head
+
+def _conf_inputs(seed, B=3, K=5, D=40, V=30, r=8):
+    rng = np.random.default_rng(seed)
+    h = S.f32_to_bf16(rng.standard_normal((B, K, D)).astype(np.float32))
+    W1 = S.f32_to_bf16((rng.standard_normal((V, r)) * 0.9).astype(np.float32))
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+    return h, W1, anchor, tokens
+
+
+def test_confidence_zero_weights_halves_and_survival_is_a_power_of_two():
+    """[DSp] "Confidence-scheduled verification": c_k = sigmoid(w^T [h_k; W1[x_{k-1}]]) and a_j = prod c_i.
+    With w = 0 every c_k is sigmoid(0) = 1/2 and a_k = 2^-(k+1), exactly."""
+    h, W1, anchor, tokens = _conf_inputs(40)
+    D, r = h.shape[2], W1.shape[1]
+    conf, surv = O.confidence(h, np.zeros(D + r, np.float32), W1, anchor, tokens)
+    assert np.all(conf == 0.5)
+    assert np.array_equal(surv, np.broadcast_to(0.5 ** np.arange(1, h.shape[1] + 1), surv.shape))
+
+
+@pytest.mark.parametrize("j", [0, 5])
+def test_confidence_predecessor_part_reads_the_previous_token(j):
+    """With the h part zero and the W1 part the unit vector e_j, c_k is the sigmoid of one weight of the
+    predecessor's row: W1[anchor, j] at k = 0 and W1[tokens[k-1], j] after (not the token at k)."""
+    h, W1, anchor, tokens = _conf_inputs(41)
+    B, K, D = h.shape
+    r = W1.shape[1]
+    w = np.zeros(D + r, np.float32)
+    w[D + j] = 1.0
+    conf, _ = O.confidence(h, w, W1, anchor, tokens)
+    Wd = S.bf16_to_f32(W1).astype(np.float64)
+    prev = np.concatenate([anchor[:, None], tokens[:, :-1]], axis=1)
+    np.testing.assert_allclose(conf, 1.0 / (1.0 + np.exp(-Wd[prev, j])), rtol=0, atol=1e-15)
+
+
+def test_confidence_hidden_part_and_symmetry():
+    """With the W1 part zero and the h part s e_i, c_k = sigmoid(s h[b, k, i]); negating w maps c to 1 - c
+    (sigmoid(-z) = 1 - sigmoid(z)), and survival is the running product, so it never increases."""
+    h, W1, anchor, tokens = _conf_inputs(42)
+    B, K, D = h.shape
+    r = W1.shape[1]
+    w = np.zeros(D + r, np.float32)
+    w[7] = 0.75
+    conf, _ = O.confidence(h, w, W1, anchor, tokens)
+    hd = S.bf16_to_f32(h).astype(np.float64)
+    np.testing.assert_allclose(conf, 1.0 / (1.0 + np.exp(-0.75 * hd[:, :, 7])), rtol=0, atol=1e-15)
+    rng = np.random.default_rng(43)
+    w = (rng.standard_normal(D + r) * 0.3).astype(np.float32)
+    c1, s1 = O.confidence(h, w, W1, anchor, tokens)
+    c2, _ = O.confidence(h, -w, W1, anchor, tokens)
+    np.testing.assert_allclose(c1 + c2, 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(s1, axis=1) <= 0)
+    np.testing.assert_allclose(s1, np.cumprod(c1, axis=1), rtol=1e-15, atol=0)
