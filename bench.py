@@ -217,6 +217,24 @@ def main():
         "back_to_back_tokens_per_s": round(B * K / (float(ms_b2b.mean()) / 1e3), 1),
         "timed_wall_s": round(wall, 4),
     }
+    if not args.no_extras:
+        # the same sampling round with the confidence head and prefix survival (synthetic hidden states, D = 4096,
+        # as the gated workload's): computed by the round kernel's finalizer waves, one position behind
+        gen = torch.Generator(device=dev).manual_seed(0xC0F)
+        hconf = torch.randn((B, K, 4096), generator=gen, device=dev).to(torch.bfloat16)
+        wconf = torch.randn((4096 + r,), generator=gen, device=dev) * 0.02
+
+        def conf_round():
+            D.dspark_markov_draft_confidence(U, W1, W2T, anchor, hconf, wconf, w2_layout=D.DSPARK_W2_VR,
+                                             mode=D.DSPARK_SAMPLE, seed=w.noise_seed, temperature=w.temperature,
+                                             workspace=ws)
+
+        conf_round()
+        cms, _ = timed_rounds(conf_round, 10)
+        extras["serving_with_confidence"] = {"round_ms": round(float(cms.mean()), 4),
+                                             "overhead_ms": round(float(cms.mean()) - ms_per_step, 4),
+                                             "hidden_bytes": int(hconf.numel() * 2)}
+        del hconf, wconf
     del U
     torch.cuda.empty_cache()
 

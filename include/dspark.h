@@ -114,6 +114,22 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         size_t workspace_bytes, void* stream);
 
 /*
+ * dspark_markov_draft plus the confidence head and prefix survival of the drafted block (DSpark overview,
+ * section "Confidence-scheduled verification"): conf[b, k] = sigmoid(w_h . h[b, k, :] + w_m . W1[x_{k-1}, :])
+ * with x_{k-1} the token drafted at position k-1 (the anchor at k = 0), and survival[b, k] = the product of
+ * conf[b, 0..k].  h [B, K, D] bf16 (16-byte aligned, D % 8 == 0); conf_w [D + r] fp32, w_h then w_m; conf and
+ * survival [B, K] fp32 outputs.  On the whole-round path the head is computed inside the same launch, one
+ * position behind the draft; otherwise by one extra launch after it.  fp32 arithmetic; a failed position
+ * (token -1) has NaN confidence and survival from there on.  Other arguments, outputs and errors as
+ * dspark_markov_draft; DSPARK_EUNSUPPORTED if D % 8 != 0.
+ */
+int dspark_markov_draft_confidence(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                                   const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                                   uint64_t seed, float temperature, const void* h, int D, const float* conf_w,
+                                   int32_t* tokens, float* logprobs, float* conf, float* survival, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Measurement variant of dspark_markov_draft (same arguments and results).  It also records HIP event
  * pairs on `stream` around every launch of the contraction kernel (one launch per round on the persistent
  * path, one per position otherwise) and around the whole call, waits for the call to finish (this call

@@ -44,6 +44,8 @@ def _load_lib():
         "dspark_markov_draft": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz, vp], i32),
         "dspark_markov_draft_timed": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz,
                                        vp, vp, vp, vp], i32),
+        "dspark_markov_draft_confidence": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, i32, vp,
+                                            vp, vp, vp, vp, vp, sz, vp], i32),
         "dspark_markov_step": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp, sz,
                                 vp], i32),
         "dspark_markov_logits": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, sz, vp], i32),
@@ -139,6 +141,36 @@ def dspark_markov_draft(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mo
                                     float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb, _stream(stream)),
            "dspark_markov_draft")
     return tokens, logprobs
+
+
+def dspark_markov_draft_confidence(U, W1, W2, anchor, h, conf_w, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY,
+                                   seed=0, temperature=1.0, want_logprobs=True, workspace=None, stream=None):
+    """Draft plus the confidence head: h [B,K,D] bf16, conf_w [D+r] fp32 (h part, then W1 part).  Returns
+    (tokens, logprobs or None, conf [B,K] fp32, survival [B,K] fp32)."""
+    _dev(U, "U", torch.float32, 3)
+    B, K, V = U.shape
+    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+    _dev(W2, "W2", W1.dtype, 2)
+    r = W1.shape[1]
+    _dev(anchor, "anchor", torch.int32, 1)
+    _dev(h, "h", torch.bfloat16, 3)
+    _dev(conf_w, "conf_w", torch.float32, 1)
+    if H is not None:
+        _dev(H, "H", torch.float32, 3)
+    D = h.shape[2]
+    if tuple(h.shape[:2]) != (B, K) or conf_w.shape[0] != D + r:
+        raise ValueError("h must be [B, K, D] and conf_w [D + r]")
+    wd = _wdtype(W1)
+    tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
+    logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device) if want_logprobs else None
+    conf = torch.empty((B, K), dtype=torch.float32, device=U.device)
+    surv = torch.empty((B, K), dtype=torch.float32, device=U.device)
+    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+    _check(_lib.dspark_markov_draft_confidence(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r,
+                                               mode, seed, float(temperature), _p(h), D, _p(conf_w), _p(tokens),
+                                               _p(logprobs), _p(conf), _p(surv), _p(ws), wsb, _stream(stream)),
+           "dspark_markov_draft_confidence")
+    return tokens, logprobs, conf, surv
 
 
 def dspark_markov_draft_timed(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY, seed=0,

@@ -223,7 +223,7 @@ bool coop_supported() {
 int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout, const int32_t* anchor,
                       const float* H, int B, int K, int V, int r, int mode, uint64_t seed, float temperature,
                       int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes, void* stream,
-                      hipEvent_t* ev, int* kernel_launches) {
+                      hipEvent_t* ev, int* kernel_launches, const ConfArgs* cf = nullptr) {
     g_err[0] = 0;
     int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
     if (rc) return rc;
@@ -281,6 +281,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.tokens = tokens;
             a.logprobs = logprobs;
             a.inv_t = 1.0f / teff;
+            if (cf) a.cf = *cf;
             a.spin_limit = 1u << 22;
             a.p_mc = ws.p_mc;
             a.p_s = ws.p_s;
@@ -303,6 +304,10 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
         if (rc) return rc;
     }
     if (kernel_launches) *kernel_launches = K;
+    if (cf) {
+        hipError_t e = launch_confidence(*cf, B, st);
+        if (e != hipSuccess) return device_fail(e, "confidence launch");
+    }
     return DSPARK_OK;
 }
 
@@ -349,6 +354,31 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         void* stream) {
     return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
                              logprobs, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dspark_markov_draft_confidence(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                                   const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                                   uint64_t seed, float temperature, const void* h, int D, const float* conf_w,
+                                   int32_t* tokens, float* logprobs, float* conf, float* survival, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!h || !conf_w || !conf || !survival) return fail(DSPARK_EINVAL, "h, conf_w, conf and survival must not be NULL");
+    if (D <= 0 || D % 8 != 0) return fail(DSPARK_EUNSUPPORTED, "the confidence head needs D %% 8 == 0 (D=%d)", D);
+    if (!aligned16(h)) return fail(DSPARK_EINVAL, "h must be 16-byte aligned");
+    ConfArgs c{};
+    c.h = (const uint16_t*)h;
+    c.D = D;
+    c.w = conf_w;
+    c.W1 = W1;
+    c.w1_bf16 = wdtype == DSPARK_BF16;
+    c.r = r;
+    c.K = K;
+    c.anchor = anchor;
+    c.tokens = tokens;
+    c.conf = conf;
+    c.survival = survival;
+    return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
+                             logprobs, workspace, workspace_bytes, stream, nullptr, nullptr, &c);
 }
 
 int dspark_markov_draft_timed(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,

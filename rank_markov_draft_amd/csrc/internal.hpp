@@ -60,6 +60,21 @@ struct ReduceArgs {
     int64_t out_stride;
 };
 
+// Confidence head c_k = sigmoid(w_h . h_k + w_m . W1[x_{k-1}]) and prefix survival a_k = prod_{i<=k} c_i.
+struct ConfArgs {
+    const uint16_t* h;          // [B, K, D] bf16, 16-byte aligned, D % 8 == 0; null: no confidence head
+    int D;
+    const float* w;             // [D + r]: the h part, then the W1 part
+    const void* W1;             // [V, r]
+    bool w1_bf16;
+    int r, K;
+    const int32_t* anchor;      // [B]
+    const int32_t* tokens;      // [B, K] drafted tokens (x_{-1} = anchor)
+    float* conf;                // [B, K]
+    float* survival;            // [B, K]
+};
+hipError_t launch_confidence(const ConfArgs& c, int B, hipStream_t st);
+
 // A whole draft round in one persistent cooperative launch (bf16, W2 stored [V, r], V % 4 == 0).
 struct RoundArgs {
     const float* U;             // U[b, k, v] at U + k * u_kstride + b * u_stride + v
@@ -79,6 +94,7 @@ struct RoundArgs {
     uint64_t* flag;             // set to seq by workgroup 0 once it has cleared winners, counters and error
     uint64_t seq;               // per-call sequence number (never 0)
     int32_t* tokens;            // [B, K] outputs, written by the kernel's finalizer waves
+    ConfArgs cf;                // optional confidence head, also computed by the finalizers
     float* logprobs;            // [B, K] or null
     float inv_t;
     float* p_mc;                // [K][G][Bpad] log-sum-exp partials (base-2 max of l c, sum)

@@ -108,6 +108,43 @@ __device__ __forceinline__ uint32_t grid_arrivals(const RoundArgs& a) {
     return tot;
 }
 
+// One wave: the confidence of (row b, position k) and the prefix survival ([DSp] "Confidence-scheduled
+// verification"): c_k = sigmoid(w_h . h_k + w_m . W1[x_{k-1}]), x_{-1} the anchor; a_k = a_{k-1} c_k.  It
+// depends on the tokens before position k only, so it can run as soon as x_{k-1} is known.
+// Tokens and survivals of earlier positions are read back with agent-scope loads (they were stored so).
+__device__ void confidence_step(const ConfArgs& c, int b, int k) {
+    const int lane = threadIdx.x & 63;
+    const int prev = (k == 0) ? c.anchor[b] : agent_load(c.tokens + (size_t)b * c.K + k - 1);
+    float z = 0.f;
+    const uint16_t* hrow = c.h + ((size_t)b * c.K + k) * c.D;
+#pragma unroll 8
+    for (int d0 = 8 * lane; d0 < c.D; d0 += 512) {
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(hrow + d0);
+        const uint32_t q4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            z = fmaf(c.w[d0 + 2 * e], bf16_to_f32((uint16_t)(q4[e] & 0xFFFFu)), z);
+            z = fmaf(c.w[d0 + 2 * e + 1], bf16_to_f32((uint16_t)(q4[e] >> 16)), z);
+        }
+    }
+    const bool ok = prev >= 0;  // a token of -1 marks a failed position
+    if (ok) {
+#pragma unroll 4
+        for (int j = lane; j < c.r; j += 64) {
+            const float wj = c.w1_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(c.W1)[(size_t)prev * c.r + j])
+                                       : static_cast<const float*>(c.W1)[(size_t)prev * c.r + j];
+            z = fmaf(c.w[c.D + j], wj, z);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if (lane == 0) {
+        const float ck = ok ? 1.0f / (1.0f + fast_exp2(-z * kLog2e)) : NAN;
+        const float before = (k == 0) ? 1.0f : agent_load(c.survival + (size_t)b * c.K + k - 1);
+        c.conf[(size_t)b * c.K + k] = ck;
+        agent_store(c.survival + (size_t)b * c.K + k, before * ck);
+    }
+}
+
 // One wave merges the G partials of (row b, position k): the pick from the winner word, the log-sum-exp over
 // the partials, the logit of the pick from the partial of the workgroup that owns its id.
 __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) {
@@ -138,7 +175,7 @@ __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) 
     }
     if (lane == 0) {
         const bool bad = timed_out || agent_load(a.error) != 0u || !found;
-        a.tokens[(size_t)b * a.K + k] = bad ? -1 : tok;
+        agent_store(a.tokens + (size_t)b * a.K + k, bad ? -1 : tok);
         if (a.logprobs) a.logprobs[(size_t)b * a.K + k] = bad ? NAN : l * a.inv_t - (mc + fast_log2(s)) * kLn2;
     }
 }
@@ -191,6 +228,9 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             wait_vmcnt<0>();
             if (lane == 0) agent_store(a.flag, a.seq);
         }
+        // c_0 needs only the anchor and h_0
+        if (a.cf.h)
+            for (int b = g; b < a.B; b += G) confidence_step(a.cf, b, 0);
         // Then, position by position, once every workgroup has finished it (this workgroup's release of the
         // next position, or the grid counters after the last one): tokens and log-probabilities of rows
         // g, g + G, ...  Until the last position this runs while the rest of the workgroup streams and
@@ -217,7 +257,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 }
             }
             if (timed_out && lane == 0) agent_store(a.error, 1u);
-            for (int b = g; b < a.B; b += G) finalize_pair(a, b, k, timed_out);
+
+            // c_{k+1} needs h_{k+1} and x_k only, so it follows the token of position k at once
+            for (int b = g; b < a.B; b += G) {
+                finalize_pair(a, b, k, timed_out);
+                if (a.cf.h && k + 1 < a.K) confidence_step(a.cf, b, k + 1);
+            }
         }
         return;
     }
@@ -628,7 +673,17 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     }
 }
 
+// The confidence head after a draft made position by position: one wave per row, positions in order.
+__global__ void __launch_bounds__(64) confidence_kernel(ConfArgs c) {
+    for (int k = 0; k < c.K; ++k) confidence_step(c, blockIdx.x, k);
+}
+
 }  // namespace
+
+hipError_t launch_confidence(const ConfArgs& c, int B, hipStream_t st) {
+    hipLaunchKernelGGL(confidence_kernel, dim3(B), dim3(64), 0, st, c);
+    return hipGetLastError();
+}
 
 int round_supported_r(int r) { return mfma_supported_r(r) && r <= 256; }
 

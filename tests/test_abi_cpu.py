@@ -90,11 +90,28 @@ def test_markov_draft_argument_errors(lib):
     assert call(ws=None) == 3
 
 
+def test_confidence_argument_errors(lib):
+    f = lib.dspark_markov_draft_confidence
+
+    def call(h=FAKE, D=64, w=FAKE, conf=FAKE, surv=FAKE, U=FAKE):
+        return f(U, FAKE, FAKE, 1, 1, FAKE, None, 4, 2, 64, 16, 0, 0, 1.0, h, D, w, FAKE, None, conf, surv, FAKE,
+                 1 << 30, None)
+
+    assert call(h=None) == 1
+    assert call(w=None) == 1
+    assert call(conf=None) == 1
+    assert call(surv=None) == 1
+    assert call(D=12) == 2 and "D % 8" in _err(lib)
+    assert call(D=0) == 2
+    assert call(h=ctypes.c_void_p(0x1008)) == 1  # not 16-byte aligned
+    assert call(U=None) == 1  # the draft's own checks still apply
+
+
 def test_selector_gate_topk_argument_errors(lib):
     s = lib.dspark_selector_draft
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 0, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 1
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 101, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 1
-    assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 8192, 16, 17, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 2
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 8192, 16, 65, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 2
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 16, 0, 0, 1.0, FAKE, None, None, None, FAKE, 8, None) == 3
     g = lib.dspark_gate
     assert g(None, FAKE, 4, 256, 32, FAKE, None) == 1
@@ -103,7 +120,7 @@ def test_selector_gate_topk_argument_errors(lib):
     t = lib.dspark_topk
     assert t(FAKE, 100, 4, 100, 0, FAKE, None, None, 0, None) == 1
     assert t(FAKE, 50, 4, 100, 4, FAKE, None, None, 0, None) == 1
-    assert t(FAKE, 8192, 4, 8192, 32, FAKE, None, None, 0, None) == 2
+    assert t(FAKE, 8192, 4, 8192, 65, FAKE, None, None, 0, None) == 2
     p = lib.dspark_pack_w2
     assert p(None, 10, 10, 1, FAKE, None) == 1
     assert p(FAKE, 10, 10, 9, FAKE, None) == 1
