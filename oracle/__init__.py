@@ -43,6 +43,10 @@ def _load():
         lib.oracle_noise_fill.argtypes = [u64, u32, u32, u32, i64, vp, vp]
         lib.oracle_gate.argtypes = [vp, vp, i32, i32, i32, vp]
         lib.oracle_confidence.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, i32, i32, vp, vp]
+        lib.oracle_schedule_greedy.argtypes = [vp, vp, i32, i32, vp]
+        lib.oracle_schedule_greedy.restype = dbl
+        lib.oracle_schedule_best.argtypes = [vp, vp, i32, i32, vp]
+        lib.oracle_schedule_best.restype = dbl
         lib.oracle_markov_draft.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, dbl,
                                             vp, vp, i32, vp, vp, vp, vp, vp]
         lib.oracle_markov_logits.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp]
@@ -145,6 +149,30 @@ def confidence(h, w, W1, anchor, tokens):
     _load().oracle_confidence(_ptr(h), D, _ptr(w), _ptr(W1), wd, r, _ptr(anchor), _ptr(tokens), B, K, _ptr(conf),
                               _ptr(surv))
     return conf, surv
+
+
+# ---------------------------------------------------------------------------------------- scheduling
+
+def schedule_greedy(a, sps):
+    """Greedy load-aware prefix scheduling: a [R, K] prefix survival (float32), sps [R (K + 1) + 1] steps per
+    second by target batch size.  Returns (lengths [R] int32, Theta)."""
+    a = _c(a, np.float32)
+    R, K = a.shape
+    sps = _c(sps, np.float32)
+    assert sps.shape == (R * (K + 1) + 1,)
+    lengths = np.empty(R, np.int32)
+    theta = _load().oracle_schedule_greedy(_ptr(a), _ptr(sps), R, K, _ptr(lengths))
+    return lengths, theta
+
+
+def schedule_best(a, sps):
+    """Brute force over all prefix-length vectors ((K + 1)^R <= 2^22): (lengths [R], best Theta)."""
+    a = _c(a, np.float32)
+    R, K = a.shape
+    sps = _c(sps, np.float32)
+    lengths = np.empty(R, np.int32)
+    theta = _load().oracle_schedule_best(_ptr(a), _ptr(sps), R, K, _ptr(lengths))
+    return lengths, theta
 
 
 # -------------------------------------------------------------------------------------------- markov

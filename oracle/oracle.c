@@ -163,6 +163,87 @@ void oracle_confidence(const uint16_t* h, int D, const float* w, const void* W1,
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* hardware-aware prefix scheduling                                                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [DSp] "Hardware-aware prefix scheduling": R requests, request r may verify a prefix of length l_r of its
+ * drafted block; the target batch is B = sum_r (1 + l_r) tokens, the expected committed tokens are
+ * R + sum_{(r,j) in S} a[r][j] (a = prefix survival), and the objective is
+ * Theta(S) = (R + sum a) * SPS(B), SPS the engine's steps-per-second table (sps[B], B = 0 .. R (K + 1)).
+ * Survival values that are not finite numbers in [0, 1] count as 0. */
+static double survival_value(float x) { return (x >= 0.0f && x <= 1.0f) ? (double)x : 0.0; }
+
+/* Extension order: survival descending, then position j ascending, then request r ascending.  Survival
+ * never increases along a request's block, so this order admits every prefix before its extension. */
+static const float* g_sched_a;
+static int g_sched_K;
+static int sched_cmp(const void* pa, const void* pb) {
+    const int x = *(const int*)pa, y = *(const int*)pb;
+    const double ax = survival_value(g_sched_a[x]), ay = survival_value(g_sched_a[y]);
+    if (ax != ay) return ax > ay ? -1 : 1;
+    const int jx = x % g_sched_K, jy = y % g_sched_K;
+    if (jx != jy) return jx < jy ? -1 : 1;
+    return (x / g_sched_K) < (y / g_sched_K) ? -1 : ((x / g_sched_K) > (y / g_sched_K) ? 1 : 0);
+}
+
+/* The greedy of the same section: start from B = R (no extension), take extensions in the order above and
+ * admit each while Theta strictly increases; stop at the first one that would not.  Writes l_r and returns
+ * Theta of the admitted set. */
+double oracle_schedule_greedy(const float* a, const float* sps, int R, int K, int32_t* lengths) {
+    const int n = R * K;
+    int* order = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) order[i] = i;
+    g_sched_a = a;
+    g_sched_K = K;
+    qsort(order, (size_t)n, sizeof(int), sched_cmp);
+    for (int r = 0; r < R; ++r) lengths[r] = 0;
+    double tokens = (double)R;
+    double theta = tokens * (double)sps[R];
+    for (int m = 0; m < n; ++m) {
+        const double t2 = (tokens + survival_value(a[order[m]])) * (double)sps[R + m + 1];
+        if (!(t2 > theta)) break;
+        tokens += survival_value(a[order[m]]);
+        theta = t2;
+        lengths[order[m] / K] += 1;
+    }
+    free(order);
+    return theta;
+}
+
+/* Brute force over every prefix-length vector l in [0, K]^R ((K + 1)^R <= 2^22): the largest Theta and,
+ * for the first vector (in lexicographic order) that reaches it, the lengths. */
+double oracle_schedule_best(const float* a, const float* sps, int R, int K, int32_t* lengths) {
+    if (R <= 0 || K < 0) return -1.0;
+    long total = 1;
+    for (int r = 0; r < R; ++r) {
+        total *= (K + 1);
+        if (total > (1L << 22)) return -1.0;
+    }
+    int* l = (int*)calloc((size_t)R, sizeof(int));
+    double best = -INFINITY;
+    for (long c = 0; c < total; ++c) {
+        long rem = c;
+        int count = 0;
+        double tokens = (double)R;
+        for (int r = R - 1; r >= 0; --r) {
+            l[r] = (int)(rem % (K + 1));
+            rem /= (K + 1);
+        }
+        for (int r = 0; r < R; ++r) {
+            count += l[r];
+            for (int j = 0; j < l[r]; ++j) tokens += survival_value(a[(size_t)r * K + j]);
+        }
+        const double theta = tokens * (double)sps[R + count];
+        if (theta > best) {
+            best = theta;
+            for (int r = 0; r < R; ++r) lengths[r] = l[r];
+        }
+    }
+    free(l);
+    return best;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* one calibrated position                                                                      */
 /* ------------------------------------------------------------------------------------------ */
 

@@ -504,3 +504,61 @@ def test_confidence_hidden_part_and_symmetry():
     np.testing.assert_allclose(c1 + c2, 1.0, rtol=0, atol=1e-14)
     assert np.all(np.diff(s1, axis=1) <= 0)
     np.testing.assert_allclose(s1, np.cumprod(c1, axis=1), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------------------------ prefix scheduling
+
+def _survival(R, K, seed):
+    rng = np.random.default_rng(seed)
+    c = rng.uniform(0.3, 0.99, (R, K))
+    return np.cumprod(c, axis=1).astype(np.float32)
+
+
+def test_schedule_constant_sps_admits_everything():
+    """[DSp] "Hardware-aware prefix scheduling": with a flat steps-per-second curve Theta is proportional to
+    the expected committed tokens R + sum a, so every extension with positive survival is admitted."""
+    a = _survival(4, 5, 1)
+    lengths, theta = O.schedule_greedy(a, np.full(4 * 6 + 1, 2.0, np.float32))
+    assert np.array_equal(lengths, np.full(4, 5))
+    assert theta == pytest.approx(2.0 * (4 + a.astype(np.float64).sum()), rel=1e-12)
+
+
+def test_schedule_cliff_admits_nothing():
+    """If the target cannot run more than R tokens per step (SPS = 0 beyond B = R) the baseline wins."""
+    R, K = 3, 4
+    sps = np.zeros(R * (K + 1) + 1, np.float32)
+    sps[: R + 1] = 1.0
+    lengths, theta = O.schedule_greedy(_survival(R, K, 2), sps)
+    assert np.array_equal(lengths, np.zeros(R)) and theta == 3.0
+
+
+def test_schedule_hand_example():
+    """SPS(B) = 1 / B makes Theta the committed tokens per target token: an extension is admitted while its
+    survival exceeds the current ratio.  R = 2, a = [[0.9, 0.5], [0.8, 0.1]]: Theta(0) = 2/2 = 1 and
+    adding 0.9 gives 2.9/3 < 1, so nothing is admitted; with SPS(B) = 1 (flat) everything is."""
+    a = np.array([[0.9, 0.5], [0.8, 0.1]], np.float32)
+    B = np.arange(0, 2 * 3 + 1, dtype=np.float64)
+    sps = np.where(B > 0, 1.0 / np.maximum(B, 1), 0).astype(np.float32)
+    lengths, theta = O.schedule_greedy(a, sps)
+    assert np.array_equal(lengths, [0, 0]) and theta == pytest.approx(1.0, rel=1e-7)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_greedy_against_brute_force(seed):
+    """For n admitted extensions the best set is the top n by survival, so the optimum is the best Theta along
+    the greedy order; the greedy stops at the first local maximum.  With a linear SPS curve Theta is
+    unimodal along that order and the greedy is optimal; with any curve it never beats the optimum."""
+    rng = np.random.default_rng(seed)
+    R, K = 4, 4
+    a = _survival(R, K, 100 + seed)
+    B = np.arange(R * (K + 1) + 1, dtype=np.float64)
+    lin = (10.0 - 0.35 * B).clip(0).astype(np.float32)
+    lg, tg = O.schedule_greedy(a, lin)
+    lb, tb = O.schedule_best(a, lin)
+    assert tg == pytest.approx(tb, rel=1e-12)
+    assert np.array_equal(lg, lb)
+    bumpy = (10.0 - 0.35 * B + 0.8 * np.sin(B * (1.3 + 0.1 * seed))).clip(0).astype(np.float32)
+    lg, tg = O.schedule_greedy(a, bumpy)
+    _, tb = O.schedule_best(a, bumpy)
+    assert tg <= tb + 1e-12
+    assert np.all(lg >= 0) and np.all(lg <= K)
