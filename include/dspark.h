@@ -202,6 +202,20 @@ size_t dspark_topk_workspace_bytes(int rows, int V, int topk);
 int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Hardware-aware prefix scheduling of drafted blocks (DSpark overview, section "Hardware-aware prefix
+ * scheduling").  R requests with prefix survivals survival[r, j] (j < K; e.g. the survival output of
+ * dspark_markov_draft_confidence); sps[B] = the target engine's steps per second at a batch of B tokens,
+ * B = 0 .. R (K + 1).  The greedy starts from B = R (no draft token verified), ranks the extensions (r, j) by
+ * survival (ties: smaller j, then smaller r; survival never increases along a block, so prefixes come
+ * first) and admits them while Theta = (R + sum of admitted survivals) * sps[R + admitted] strictly
+ * increases.  lengths [R] int32 output: tokens of each block to verify; theta [1] fp32 output or NULL:
+ * Theta of the admitted set.  Survival values outside [0, 1] (or NaN) count as 0.  Device pointers; one
+ * workgroup, fp64 sums.  R K <= 4096 (DSPARK_EUNSUPPORTED otherwise).
+ */
+int dspark_schedule_prefixes(const float* survival, const float* sps, int R, int K, int32_t* lengths, float* theta,
+                             void* stream);
+
 /* Workspace bytes dspark_selector_draft needs (0 on bad sizes). */
 size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk);
 

@@ -54,6 +54,7 @@ def _load_lib():
         "dspark_topk_workspace_bytes": ([i32, i32, i32], sz),
         "dspark_topk": ([vp, i64, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "dspark_selector_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+        "dspark_schedule_prefixes": ([vp, vp, i32, i32, vp, vp, vp], i32),
         "dspark_selector_draft": ([vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp, vp, sz,
                                    vp], i32),
     }
@@ -285,6 +286,21 @@ def dspark_topk(U, topk, *, want_values=True, stream=None):
 
 def dspark_selector_workspace_bytes(B, K, V, r, topk) -> int:
     return int(_lib.dspark_selector_workspace_bytes(B, K, V, r, topk))
+
+
+def dspark_schedule_prefixes(survival, sps, *, stream=None):
+    """Greedy load-aware prefix scheduling.  survival [R, K] fp32, sps [R (K + 1) + 1] fp32 (steps per second by
+    target batch size).  Returns (lengths [R] int32, theta [1] fp32)."""
+    _dev(survival, "survival", torch.float32, 2)
+    R, K = survival.shape
+    _dev(sps, "sps", torch.float32, 1)
+    if sps.shape[0] != R * (K + 1) + 1:
+        raise ValueError("sps must have R (K + 1) + 1 entries")
+    lengths = torch.empty((R,), dtype=torch.int32, device=survival.device)
+    theta = torch.empty((1,), dtype=torch.float32, device=survival.device)
+    _check(_lib.dspark_schedule_prefixes(_p(survival), _p(sps), R, K, _p(lengths), _p(theta), _stream(stream)),
+           "dspark_schedule_prefixes")
+    return lengths, theta
 
 
 def dspark_selector_draft(U, A, Bemb, anchor, *, H=None, topk=16, mode=DSPARK_GREEDY, seed=0, temperature=1.0,

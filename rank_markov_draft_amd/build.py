@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 OUT = os.path.join(OUT_DIR, "libdspark.so")
-SOURCES = ["api.hip", "markov.hip", "markov_round.hip", "selector.hip", "gate.hip", "util.hip"]
+SOURCES = ["api.hip", "markov.hip", "markov_round.hip", "selector.hip", "gate.hip", "schedule.hip", "util.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep hipcc from forming packed fp32 instructions by itself

@@ -507,6 +507,17 @@ int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int
     return DSPARK_OK;
 }
 
+int dspark_schedule_prefixes(const float* survival, const float* sps, int R, int K, int32_t* lengths, float* theta,
+                             void* stream) {
+    g_err[0] = 0;
+    if (!survival || !sps || !lengths) return fail(DSPARK_EINVAL, "survival, sps and lengths must not be NULL");
+    if (R <= 0 || K <= 0) return fail(DSPARK_EINVAL, "R and K must be positive");
+    if (!schedule_supported(R, K)) return fail(DSPARK_EUNSUPPORTED, "R * K = %ld exceeds 4096", (long)R * K);
+    hipError_t e = launch_schedule(survival, sps, R, K, lengths, theta, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "schedule launch");
+    return DSPARK_OK;
+}
+
 size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk) {
     if (B <= 0 || K <= 0 || V <= 0 || r <= 0 || topk <= 0) return 0;
     const size_t tstride = (size_t)topk + (size_t)(K - 1) * topk * topk;

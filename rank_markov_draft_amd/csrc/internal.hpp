@@ -147,4 +147,7 @@ hipError_t launch_walk(const SelectorArgs& a, hipStream_t st);
 
 int device_cu_count();
 
+int schedule_supported(int R, int K);
+hipError_t launch_schedule(const float* a, const float* sps, int R, int K, int32_t* lengths, float* theta, hipStream_t st);
+
 }  // namespace dspark

@@ -107,6 +107,14 @@ def test_confidence_argument_errors(lib):
     assert call(U=None) == 1  # the draft's own checks still apply
 
 
+def test_schedule_argument_errors(lib):
+    f = lib.dspark_schedule_prefixes
+    assert f(None, FAKE, 4, 4, FAKE, None, None) == 1
+    assert f(FAKE, FAKE, 0, 4, FAKE, None, None) == 1
+    assert f(FAKE, FAKE, 4, 0, FAKE, None, None) == 1
+    assert f(FAKE, FAKE, 128, 64, FAKE, None, None) == 2 and "4096" in _err(lib)
+
+
 def test_selector_gate_topk_argument_errors(lib):
     s = lib.dspark_selector_draft
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 0, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 1
