@@ -234,6 +234,18 @@ def main():
         extras["serving_with_confidence"] = {"round_ms": round(float(cms.mean()), 4),
                                              "overhead_ms": round(float(cms.mean()) - ms_per_step, 4),
                                              "hidden_bytes": int(hconf.numel() * 2)}
+        # verify lengths from the block's survival: greedy load-aware prefix scheduling over a synthetic
+        # steps-per-second curve (flat up to a knee, then falling as 1/B)
+        _, _, _, surv = D.dspark_markov_draft_confidence(U, W1, W2T, anchor, hconf, wconf, w2_layout=D.DSPARK_W2_VR,
+                                                         mode=D.DSPARK_SAMPLE, seed=w.noise_seed,
+                                                         temperature=w.temperature, workspace=ws)
+        bsz = torch.arange(B * (K + 1) + 1, device=dev, dtype=torch.float32)
+        knee = float(B * 4)
+        sps = torch.where(bsz <= knee, torch.full_like(bsz, 40.0), 40.0 * knee / bsz.clamp(min=1.0))
+        lengths, theta = D.dspark_schedule_prefixes(surv, sps)
+        sched_ms, _ = timed_rounds(lambda: D.dspark_schedule_prefixes(surv, sps), 20, flush=False)
+        extras["prefix_schedule"] = {"R": B, "K": K, "call_ms": round(float(sched_ms.mean()), 4),
+                                     "verified_tokens": int(lengths.sum().item()), "theta": round(float(theta.item()), 2)}
         del hconf, wconf
     del U
     torch.cuda.empty_cache()
