@@ -209,12 +209,23 @@ def main():
     # back-to-back rounds without eviction (W2 may stay in the last-level cache across rounds)
     ms_b2b, _ = timed_rounds(serving_round, args.steps, flush=False)
 
+    # the same round captured once in a graph and replayed (evicted like the plain enqueue)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=side):
+        serving_round()
+    torch.cuda.synchronize()
+    ms_graph, _ = timed_rounds(graph.replay, args.steps)
+
     extras = {
         "round_ms_p10": round(float(np.percentile(ms, 10)), 4), "round_ms_p90": round(float(np.percentile(ms, 90)), 4),
         "pct_of_hbm_roofline": round(100.0 * roof_round_ms / ms_per_step, 2),
         "roofline_tokens_per_s": round(roof_tok_s, 1), "roofline_round_ms": round(roof_round_ms, 4),
         "back_to_back_round_ms": round(float(ms_b2b.mean()), 4),
         "back_to_back_tokens_per_s": round(B * K / (float(ms_b2b.mean()) / 1e3), 1),
+        "graph_replay_round_ms": round(float(ms_graph.mean()), 4),
+        "graph_replay_tokens_per_s": round(B * K / (float(ms_graph.mean()) / 1e3), 1),
         "timed_wall_s": round(wall, 4),
     }
     if not args.no_extras:
