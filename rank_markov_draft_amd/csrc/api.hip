@@ -57,9 +57,10 @@ int round_gmax() {
 
 constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines), the error word, the init flag
 
-// Sequence numbers of whole-round launches: the kernel clears its own counters and marks the clearing with
-// the call's number, so a stale flag left in a reused workspace by an earlier call never matches.  The
-// start is drawn from the clock so that two processes sharing memory are unlikely to collide.
+// Sequence numbers of whole-round launches: the kernel clears its own counters and marks the clearing with a
+// value made from the call's number and the workspace's launch epoch (advanced by every launch, so replays of
+// a captured graph, whose arguments are fixed, differ too); a stale flag never matches.  The start is drawn
+// from the clock so that two processes sharing memory are unlikely to collide.
 uint64_t next_call_seq() {
     static std::atomic<uint64_t> seq{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
     uint64_t s;
@@ -277,6 +278,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.barrier = ws.counters;
             a.error = ws.counters + 256;  // after the 8 counter lines (32 words apart)
             a.flag = reinterpret_cast<uint64_t*>(ws.counters + 288);
+            a.epoch = ws.counters + 320;
             a.seq = next_call_seq();
             a.tokens = tokens;
             a.logprobs = logprobs;

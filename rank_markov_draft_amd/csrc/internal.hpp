@@ -91,8 +91,9 @@ struct RoundArgs {
     uint32_t* barrier;          // grid barrier counter
     uint32_t* error;            // set if a barrier wait timed out
     uint32_t spin_limit;
-    uint64_t* flag;             // set to seq by workgroup 0 once it has cleared winners, counters and error
-    uint64_t seq;               // per-call sequence number (never 0)
+    uint64_t* flag;             // set by workgroup 0 once it has cleared winners, counters and error
+    uint32_t* epoch;            // launches of the workspace so far; advanced at the end of every launch
+    uint64_t seq;               // per-call sequence number (never 0); with the epoch it names the launch
     int32_t* tokens;            // [B, K] outputs, written by the kernel's finalizer waves
     ConfArgs cf;                // optional confidence head, also computed by the finalizers
     float* logprobs;            // [B, K] or null

@@ -101,6 +101,23 @@ __device__ __forceinline__ void agent_store(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The flag value that names this launch: the call's sequence number mixed with the workspace's epoch.
+__device__ __forceinline__ uint64_t launch_tag(const RoundArgs& a, uint32_t ep) {
+    return a.seq ^ (0x9E3779B97F4A7C15ull * ((uint64_t)ep + 1ull));
+}
+
+// Waits (one lane) until workgroup 0 has cleared this launch's counters; bounded.
+__device__ __forceinline__ void wait_cleared(const RoundArgs& a, uint64_t tag) {
+    uint32_t spins = 0;
+    while (agent_load(a.flag) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+            __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t grid_arrivals(const RoundArgs& a) {
     uint32_t tot = 0;
 #pragma unroll
@@ -214,6 +231,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         stepdone = 0u;
         released = 0u;
     }
+    // every wave reads the epoch before workgroup 0 can advance it (at the very end of the launch)
+    const uint64_t tag = launch_tag(a, agent_load(a.epoch));
     __syncthreads();
 
     if (wave >= kConsumers + kProducers) {
@@ -226,7 +245,9 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             if (lane < kNumCounters) agent_store(a.barrier + kCounterStride * lane, 0u);
             if (lane == 0) agent_store(a.error, 0u);
             wait_vmcnt<0>();
-            if (lane == 0) agent_store(a.flag, a.seq);
+            if (lane == 0) agent_store(a.flag, tag);
+        } else if (lane == 0) {
+            wait_cleared(a, tag);  // the counters it polls after the last position must be this launch's
         }
         // c_0 needs only the anchor and h_0
         if (a.cf.h)
@@ -264,6 +285,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 if (a.cf.h && k + 1 < a.K) confidence_step(a.cf, b, k + 1);
             }
         }
+        // every workgroup has arrived after its last position, so all have read the epoch: advance it
+        if (g == 0 && lane == 0) agent_store(a.epoch, agent_load(a.epoch) + 1u);
         return;
     }
     if (wave >= kConsumers) {
@@ -637,17 +660,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 lbest = ol;
             }
             lse_merge(mc2, s2, omc, os);
-            if (seg == 0 && lane == 0) {
-                // the winner words and counters of this call are cleared before the first atomics touch them
-                uint32_t spins = 0;
-                while (agent_load(a.flag) != a.seq) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++spins > spin_limit) {
-                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-            }
+            // the winner words and counters of this launch are cleared before the first atomics touch them
+            if (seg == 0 && lane == 0) wait_cleared(a, tag);
             if (half == 0 && valid_b) {
                 const unsigned long long packed =
                     ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
