@@ -7,7 +7,7 @@
 // ranks the extensions by survival (ties: position, then request; survival never increases along a block,
 // so every prefix comes before its extension) and admits them while Theta strictly increases.
 //
-// One workgroup: a bitonic sort of the R K extensions in LDS, fp64 prefix sums of the sorted survivals,
+// One workgroup: a bitonic sort of the R K extensions (registers, shuffles and LDS), fp64 prefix sums of the sorted survivals,
 // Theta for every admitted count, the first count whose successor does not increase Theta, and the
 // per-request counts of the admitted extensions.  R K <= 4096.
 #include "internal.hpp"
@@ -23,13 +23,9 @@ constexpr int kSchedPer = kSchedMax / kSchedThreads;
 // survival values that are not numbers in [0, 1] count as 0
 __device__ __forceinline__ float survival_value(float x) { return (x >= 0.f && x <= 1.f) ? x : 0.f; }
 
-// extension order: survival desc, position j asc, request r asc (ids i = r K + j are unique)
-__device__ __forceinline__ bool ext_before(float ka, int ia, float kb, int ib, int K) {
-    if (ka != kb) return ka > kb;
-    const int ja = ia % K, jb = ib % K;
-    if (ja != jb) return ja < jb;
-    return ia / K < ib / K;
-}
+// extension order: survival desc, then position j asc, then request r asc.  Entries carry the tie-break
+// key q = j R + r (unique), so the comparison needs no division.
+__device__ __forceinline__ bool ext_before(float ka, int qa, float kb, int qb) { return ka != kb ? ka > kb : qa < qb; }
 
 __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(const float* __restrict__ a, const float* __restrict__ sps,
                                                                  int R, int K, int32_t* __restrict__ lengths,
@@ -40,38 +36,101 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(const float* __
     __shared__ int counts[kSchedMax];
     __shared__ int nstop;
     const int t = threadIdx.x;
+    const int lane = t & 63;
     const int n = R * K;
-    int np = 1;
+    int np = kSchedThreads;  // at least one entry per thread; padding sorts last
     while (np < n) np <<= 1;
-    for (int i = t; i < np; i += kSchedThreads) {
-        key[i] = i < n ? survival_value(a[i]) : -1.f;  // padding sorts last
-        id[i] = i < n ? i : 0x7FFFFFFF;
+    const int E = np / kSchedThreads;  // 1, 2 or 4 entries per thread, thread t holds positions t E .. t E + E - 1
+    float kv[kSchedPer];
+    int iv[kSchedPer];
+#pragma unroll
+    for (int e = 0; e < kSchedPer; ++e) {
+        const int i = t * E + e;
+        kv[e] = (e < E && i < n) ? survival_value(a[i]) : -1.f;
+        iv[e] = (e < E && i < n) ? (i % K) * R + i / K : 0x7FFFFFFF;  // i = r K + j  ->  j R + r
     }
     for (int i = t; i < R; i += kSchedThreads) counts[i] = 0;
     if (t == 0) nstop = n;
-    __syncthreads();
+    // (x, ix) comes before (y, iy); padding (id INT_MAX) after everything
+    auto first = [&](float x, int ix, float y, int iy) {
+        if (iy == 0x7FFFFFFF) return ix != 0x7FFFFFFF;
+        if (ix == 0x7FFFFFFF) return false;
+        return ext_before(x, ix, y, iy);
+    };
+    // Bitonic network in registers: strides inside a thread swap registers, strides inside a wave use
+    // shuffles, only strides across waves go through LDS (two barriers each).  In a pair (i, j = i ^ stride)
+    // of an ascending block the lower index keeps the element that comes first.
     for (int size = 2; size <= np; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = t; i < np; i += kSchedThreads) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool up = (i & size) == 0;
-                    const bool jb = (id[j] == 0x7FFFFFFF) ? false
-                                    : (id[i] == 0x7FFFFFFF) ? true
-                                                            : ext_before(key[j], id[j], key[i], id[i], K);
-                    if (up ? jb : !jb) {
-                        const float tk = key[i];
-                        const int ti = id[i];
-                        key[i] = key[j];
-                        id[i] = id[j];
-                        key[j] = tk;
-                        id[j] = ti;
+            if (stride < E) {
+#pragma unroll
+                for (int e = 0; e < kSchedPer; ++e) {
+                    const int f = e ^ stride;
+                    if (e < E && f > e) {
+                        const int i = t * E + e;
+                        const bool up = (i & size) == 0;
+                        const bool ff = first(kv[f], iv[f], kv[e], iv[e]);
+                        if (up ? ff : !ff) {
+                            const float tk = kv[e];
+                            const int ti = iv[e];
+                            kv[e] = kv[f];
+                            iv[e] = iv[f];
+                            kv[f] = tk;
+                            iv[f] = ti;
+                        }
                     }
                 }
+            } else if (stride < 64 * E) {
+                const int delta = stride / E;
+#pragma unroll
+                for (int e = 0; e < kSchedPer; ++e) {
+                    const float pk = __shfl_xor(kv[e], delta);
+                    const int pi = __shfl_xor(iv[e], delta);
+                    if (e < E) {
+                        const int i = t * E + e;
+                        const bool lower = (lane & delta) == 0;
+                        const bool up = (i & size) == 0;
+                        const bool pf = first(pk, pi, kv[e], iv[e]);
+                        if (lower == up ? pf : !pf) {
+                            kv[e] = pk;
+                            iv[e] = pi;
+                        }
+                    }
+                }
+            } else {
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kSchedPer; ++e)
+                    if (e < E) {
+                        key[t * E + e] = kv[e];
+                        id[t * E + e] = iv[e];
+                    }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kSchedPer; ++e)
+                    if (e < E) {
+                        const int i = t * E + e;
+                        const int j = i ^ stride;
+                        const float pk = key[j];
+                        const int pi = id[j];
+                        const bool up = (i & size) == 0;
+                        const bool pf = first(pk, pi, kv[e], iv[e]);
+                        if ((i < j) == up ? pf : !pf) {
+                            kv[e] = pk;
+                            iv[e] = pi;
+                        }
+                    }
             }
-            __syncthreads();
         }
     }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSchedPer; ++e)
+        if (e < E) {
+            key[t * E + e] = kv[e];
+            id[t * E + e] = iv[e];
+        }
+    __syncthreads();
     // exclusive prefix sums S_m = sum_{q < m} key[q]: per-thread chunks, then a scan of the chunk sums
     double local[kSchedPer];
     double acc = 0.0;
@@ -103,13 +162,18 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(const float* __
     }
     __syncthreads();
     const int ns = nstop;
-    for (int m = t; m < ns; m += kSchedThreads) atomicAdd(&counts[id[m] / K], 1);
+    for (int m = t; m < ns; m += kSchedThreads) atomicAdd(&counts[id[m] % R], 1);
     __syncthreads();
     for (int r = t; r < R; r += kSchedThreads) lengths[r] = counts[r];
-    if (theta_out && t == 0) {
-        double s = 0.0;
-        for (int m = 0; m < ns; ++m) s += (double)key[m];
-        *theta_out = (float)(((double)R + s) * (double)sps[R + ns]);
+    if (theta_out) {
+        // Theta of the admitted set from the prefix sums: the thread whose chunk holds position ns, or the
+        // total when every slot is admitted
+        if (ns < kSchedMax && ns / kSchedPer == t) {
+            const double sn = base + local[ns - t * kSchedPer];
+            *theta_out = (float)(((double)R + sn) * (double)sps[R + ns]);
+        } else if (ns == kSchedMax && t == 0) {
+            *theta_out = (float)(((double)R + part[kSchedThreads - 1]) * (double)sps[R + ns]);
+        }
     }
 }
 
