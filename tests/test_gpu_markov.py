@@ -187,3 +187,40 @@ def test_full_serving_logits_sampled_rows(D, serving):
 def test_full_batch1_greedy(D):
     w = S.workload("batch1")
     _full_draft_check(D, w, [0], S.GREEDY, 0)
+
+
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+def test_many_row_blocks(D, mode):
+    """B = 512: four 128-row blocks per position on the whole-round path (each block is a segment of its own
+    with the predecessors of the same position)."""
+    w = S.strong("serving", B=512, K=3, V=2048, r=64, mode=mode)
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), w2_layout=D.DSPARK_W2_VR,
+                                    mode=mode, seed=w.noise_seed)
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=w.noise_seed, follow=tok)
+    check_draft(tok, lp, ref, what="B512")
+
+
+def test_all_logits_equal(D):
+    """Degenerate rows: U constant and W2 = 0, so every id ties.  Greedy takes the lowest id at every
+    position and its log-probability is -ln V (closed form); the pick keeps the lowest id across lanes,
+    tiles and workgroups alike."""
+    B, K, V, r = 130, 3, 4000, 64
+    U = np.full((B, K, V), 1.25, np.float32)
+    W1 = S.f32_to_bf16(np.ones((V, r), np.float32))
+    W2T = np.zeros((V, r), np.uint16)
+    anchor = np.arange(B, dtype=np.int32) % V
+    tok, lp = D.dspark_markov_draft(t_f32(U), t_w(W1), t_w(W2T), t_i32(anchor), w2_layout=D.DSPARK_W2_VR)
+    assert np.all(host(tok) == 0)
+    np.testing.assert_allclose(host(lp), -np.log(V), rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("T", [0.05, 10.0])
+def test_sampling_temperature_extremes(D, T):
+    """Very sharp and very flat sampling both follow the oracle (keys l / T + G, log softmax of l / T)."""
+    w = S.strong("serving", B=24, K=4, V=3000, r=64, mode=S.SAMPLE)
+    tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), w2_layout=D.DSPARK_W2_VR,
+                                    mode=D.DSPARK_SAMPLE, seed=99, temperature=T)
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=99, temperature=T, follow=tok)
+    check_draft(tok, lp, ref, what=f"T={T}")
