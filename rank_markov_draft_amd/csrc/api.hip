@@ -55,7 +55,12 @@ int round_gmax() {
     return n < kMaxG ? n : kMaxG;
 }
 
-constexpr size_t kCounterBytes = 2048;  // grid-barrier counters (8 cache lines), the error word, the init flag
+// grid-barrier group counters (8 cache lines), the error word, the init flag, the epoch, the top counter and
+// the 8 release words
+constexpr size_t kCounterBytes = 4096;
+constexpr int kErrorWord = 256, kFlagWord = 288, kEpochWord = 320, kTopWord = 352, kReleaseWord = 512;
+static_assert(kCounterStride * kBarrierGroups <= kErrorWord, "group counters overlap the error word");
+static_assert((kReleaseWord + kCounterStride * kBarrierGroups) * 4 <= (int)kCounterBytes, "release words overflow");
 
 // Sequence numbers of whole-round launches: the kernel clears its own counters and marks the clearing with a
 // value made from the call's number and the workspace's launch epoch (advanced by every launch, so replays of
@@ -68,10 +73,10 @@ uint64_t next_call_seq() {
     return s;
 }
 
-// winners [K][Bpad] u64 (kWinnerStride words apart), the counters, four [K][Gmax][Bpad] partial arrays
+// winners [K][Bpad][kWinnerSlots] u64 (kWinnerStride words apart), the counters, four [K][Gmax][Bpad] partial arrays
 size_t round_region_bytes(int B, int K) {
     const size_t Bpad = (size_t)round_up(B, kRowPad);
-    return align256(sizeof(unsigned long long) * (size_t)K * Bpad * kWinnerStride) + kCounterBytes +
+    return align256(sizeof(unsigned long long) * (size_t)K * Bpad * kWinnerSlots * kWinnerStride) + kCounterBytes +
            4 * align256(sizeof(float) * (size_t)K * round_gmax() * Bpad);
 }
 
@@ -92,7 +97,7 @@ MarkovWs carve_markov(void* ws, int B, int K) {
     w.part.m = (float*)(p + 3 * one);
     w.part.s = (float*)(p + 4 * one);
     uint8_t* q = p + 5 * one;
-    const size_t wn = align256(sizeof(unsigned long long) * (size_t)K * w.Bpad * kWinnerStride);
+    const size_t wn = align256(sizeof(unsigned long long) * (size_t)K * w.Bpad * kWinnerSlots * kWinnerStride);
     w.winners = (unsigned long long*)q;
     w.counters = (uint32_t*)(q + wn);
     const size_t pn = align256(sizeof(float) * (size_t)K * round_gmax() * w.Bpad);
@@ -276,9 +281,11 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.Bpad = ws.Bpad;
             a.winners = ws.winners;
             a.barrier = ws.counters;
-            a.error = ws.counters + 256;  // after the 8 counter lines (32 words apart)
-            a.flag = reinterpret_cast<uint64_t*>(ws.counters + 288);
-            a.epoch = ws.counters + 320;
+            a.error = ws.counters + kErrorWord;
+            a.flag = reinterpret_cast<uint64_t*>(ws.counters + kFlagWord);
+            a.epoch = ws.counters + kEpochWord;
+            a.top = ws.counters + kTopWord;
+            a.release = ws.counters + kReleaseWord;
             a.seq = next_call_seq();
             a.tokens = tokens;
             a.logprobs = logprobs;

@@ -87,8 +87,10 @@ struct RoundArgs {
     uint32_t k0;
     float c;                    // log2(e) / T
     int ntiles, G, Bpad;
-    unsigned long long* winners;  // [K][Bpad] packed (ordered key, ~id), kWinnerStride words apart
-    uint32_t* barrier;          // grid barrier counter
+    unsigned long long* winners;  // [K][Bpad][kWinnerSlots] packed (ordered key, ~id), kWinnerStride words apart
+    uint32_t* barrier;          // grid barrier: kBarrierGroups group arrival counters, one cache line each
+    uint32_t* top;              // arrivals of whole groups
+    uint32_t* release;          // kBarrierGroups copies of the last released position, one cache line each
     uint32_t* error;            // set if a barrier wait timed out
     uint32_t spin_limit;
     uint64_t* flag;             // set by workgroup 0 once it has cleared winners, counters and error
@@ -103,9 +105,17 @@ struct RoundArgs {
     int* p_idx;                 // [K][G][Bpad] best id and its logit per workgroup
     float* p_l;
 };
-// Each (position, row) winner word has a 128-byte line of its own: every workgroup updates every row's word
-// once per position, and words sharing a line would serialise those atomics.
+// Each (position, row) pick has kWinnerSlots words (workgroup g updates slot g % kWinnerSlots), each on a
+// 128-byte line of its own: every workgroup updates every row once per position, and atomics on one line are
+// serialised where they are performed, so fewer updates per line shorten the end of a position.  A reader
+// takes the largest slot.
 constexpr int kWinnerStride = 16;
+constexpr int kWinnerSlots = 2;
+// Grid barrier: workgroup g arrives on group counter g % kBarrierGroups; the last arrival of a group counts
+// on the top counter, and the last arrival there writes every copy of the release word, which each workgroup
+// polls on a line shared with few others.
+constexpr int kBarrierGroups = 8;
+constexpr int kCounterStride = 32;  // words between counters (128 bytes)
 int round_supported_r(int r);
 int round_lds_bytes(int r);
 int round_max_coresident(int r, bool sample, bool gated);

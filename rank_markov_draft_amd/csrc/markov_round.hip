@@ -23,9 +23,13 @@
 //    MFMAs of tile t + 1 are issued inside the epilogue of tile t.  No logits are written.
 //  * Sampling uses the exponential-race form of Gumbel-max: argmax_v p_v / E_v with p_v = 2^(l_v c - m) (the
 //    same exponential the log-sum-exp needs) and E_v = -log2 u_v, which is argmax_v (l_v / T + G_v) exactly.
-//  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id) gives the global
-//    pick with ties to the lower id; log-sum-exp partials go to the workspace.  A grid barrier (counter,
-//    bounded spin) then releases the next position, whose workgroups gather W1 rows of the new tokens.
+//  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id), spread over two
+//    words per row, gives the global pick with ties to the lower id; log-sum-exp partials go to the
+//    workspace.  A grid barrier then releases the next position, whose workgroups gather W1 rows of the new
+//    tokens.  The barrier is a two-level arrival tree (8 group counters, then a top counter) whose last
+//    arrival writes 8 copies of a release word: every poll reads one line shared by an eighth of the grid, and
+//    the polls do not queue behind the arrivals as they did on counters polled by the whole grid (the
+//    boundary took about twice as long so).
 //  * A ninth wave per workgroup (the finalizer) clears the pick words and counters at the start of the launch
 //    and, one position behind, merges the log-sum-exp partials of its rows into tokens and log-probabilities,
 //    so a round is a single launch.
@@ -89,9 +93,6 @@ __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-constexpr int kNumCounters = 8;  // the grid barrier counter is spread over 8 cache lines
-constexpr int kCounterStride = 32;
-
 template <typename T>
 __device__ __forceinline__ T agent_load(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -118,11 +119,34 @@ __device__ __forceinline__ void wait_cleared(const RoundArgs& a, uint64_t tag) {
     }
 }
 
-__device__ __forceinline__ uint32_t grid_arrivals(const RoundArgs& a) {
-    uint32_t tot = 0;
+// The last position every workgroup has finished, as this workgroup's copy of the release word shows.
+__device__ __forceinline__ uint32_t released_position(const RoundArgs& a) {
+    return agent_load(a.release + kCounterStride * (blockIdx.x % kBarrierGroups));
+}
+
+// The pick word of (position k, row b): the largest of its slots.
+__device__ __forceinline__ unsigned long long pick_word(const RoundArgs& a, int k, int b) {
+    const unsigned long long* w = a.winners + ((size_t)k * a.Bpad + b) * kWinnerSlots * kWinnerStride;
+    unsigned long long v[kWinnerSlots];
 #pragma unroll
-    for (int cc = 0; cc < kNumCounters; ++cc) tot += agent_load(a.barrier + kCounterStride * cc);
-    return tot;
+    for (int s = 0; s < kWinnerSlots; ++s) v[s] = agent_load(w + s * kWinnerStride);
+    unsigned long long best = v[0];
+#pragma unroll
+    for (int s = 1; s < kWinnerSlots; ++s) best = v[s] > best ? v[s] : best;
+    return best;
+}
+
+// Arrival of this workgroup at the end of position k (one lane of its last consumer wave, after the wave's
+// picks are performed).  Returns true for the grid's last arrival, which then releases the position.
+__device__ __forceinline__ bool arrive(const RoundArgs& a, int k) {
+    const int G = gridDim.x;
+    const int grp = (int)blockIdx.x % kBarrierGroups;
+    const uint32_t members = (uint32_t)((G - grp + kBarrierGroups - 1) / kBarrierGroups);
+    const uint32_t groups = (uint32_t)min(G, kBarrierGroups);
+    const uint32_t old = __hip_atomic_fetch_add(a.barrier + kCounterStride * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old != members * (uint32_t)(k + 1) - 1u) return false;
+    const uint32_t o2 = __hip_atomic_fetch_add(a.top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return o2 == groups * (uint32_t)(k + 1) - 1u;
 }
 
 // One wave: the confidence of (row b, position k) and the prefix survival ([DSp] "Confidence-scheduled
@@ -167,7 +191,7 @@ __device__ void confidence_step(const ConfArgs& c, int b, int k) {
 __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) {
     const int lane = threadIdx.x & 63;
     const int G = a.G;
-    const unsigned long long wv = agent_load(a.winners + ((size_t)k * a.Bpad + b) * kWinnerStride);
+    const unsigned long long wv = pick_word(a, k, b);
     const int tok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
     float mc = kMinFinite, s = 0.f, l = 0.f;
     int found = 0;
@@ -240,10 +264,16 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         // Workgroup 0 first clears the winner words, the grid counters and the error word, then publishes the
         // call's sequence number; consumers check it before their first atomics.  No other launch is needed.
         if (g == 0) {
-            const size_t nw = (size_t)a.K * a.Bpad;
+            const size_t nw = (size_t)a.K * a.Bpad * kWinnerSlots;
             for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i * kWinnerStride, 0ull);
-            if (lane < kNumCounters) agent_store(a.barrier + kCounterStride * lane, 0u);
-            if (lane == 0) agent_store(a.error, 0u);
+            if (lane < kBarrierGroups) {
+                agent_store(a.barrier + kCounterStride * lane, 0u);
+                agent_store(a.release + kCounterStride * lane, 0u);
+            }
+            if (lane == 0) {
+                agent_store(a.top, 0u);
+                agent_store(a.error, 0u);
+            }
             wait_vmcnt<0>();
             if (lane == 0) agent_store(a.flag, tag);
         } else if (lane == 0) {
@@ -253,7 +283,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         if (a.cf.h)
             for (int b = g; b < a.B; b += G) confidence_step(a.cf, b, 0);
         // Then, position by position, once every workgroup has finished it (this workgroup's release of the
-        // next position, or the grid counters after the last one): tokens and log-probabilities of rows
+        // next position, or the release word after the last one): tokens and log-probabilities of rows
         // g, g + G, ...  Until the last position this runs while the rest of the workgroup streams and
         // computes, off the serial path.
         for (int k = 0; k < a.K; ++k) {
@@ -268,8 +298,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                     }
                 }
             } else {
-                const uint32_t target = (uint32_t)G * (uint32_t)a.K;
-                while (grid_arrivals(a) < target) {
+                while (released_position(a) < (uint32_t)a.K) {
                     __builtin_amdgcn_s_sleep(1);
                     if (++spins > spin_limit) {
                         timed_out = true;
@@ -496,15 +525,25 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     // nxt), so the matrix cores' dependent accumulation chain runs under the vector ALUs' work.
     auto pipelined = [&](f32x16_t& cur, f32x16_t& nxt, int i, int t) {
         const std::integral_constant<bool, false> kUnmasked{};
+        // The next tile's reads first (its U tile and the first two A operands), then the head of this tile's
+        // epilogue while they land.  Then, per element, the A operand two MFMAs ahead, one MFMA and the
+        // element's vector work.  The scheduling barriers keep that order: left alone, the scheduler reads each
+        // A operand right before its MFMA and stalls the wave on every read.
+        nxt = read_u(i + 1);
+        bf16x8_t fr[RK];
+        fr[0] = frag(i + 1, 0);
+        if (RK > 1) fr[1] = frag(i + 1, 1);
+        if (SAMPLE) __builtin_amdgcn_sched_barrier(0);
         float mc;
         const float cm = tile_head(cur, t, kUnmasked, mc);
         const uint32_t yb = SAMPLE ? noise_base(t) : 0u;
-        nxt = read_u(i + 1);
         bool improved = false;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (j < RK) nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i + 1, j), xf[j], nxt, 0, 0, 0);
+            if (j + 2 < RK) fr[j + 2] = frag(i + 1, j + 2);
+            if (j < RK) nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], xf[j], nxt, 0, 0, 0);
             tile_elem(cur, j, mc, yb, improved);
+            if (SAMPLE) __builtin_amdgcn_sched_barrier(0);
         }
         if (SAMPLE) btile = improved ? t : btile;
         else greedy_pick(cur, cm, t);
@@ -530,13 +569,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         const bool wave_live = rb * kRRows + wave * 32 < a.B;
 
         // a new position (or row block): wait for the previous position's picks, then gather X.  Consumer wave 0
-        // polls the grid counters; the other consumer waves wait for its LDS flag.
+        // polls this workgroup's copy of the release word; the other consumer waves wait for its LDS flag.
         if (k > 0 && rb == 0) {
             if (wave == 0) {
-                const uint32_t target = (uint32_t)G * (uint32_t)k;
                 uint32_t spins = 0;
                 while (true) {
-                    if (grid_arrivals(a) >= target) break;
+                    if (released_position(a) >= (uint32_t)k) break;
                     __builtin_amdgcn_s_sleep(1);
                     if (++spins > spin_limit) {
                         __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -561,8 +599,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 if (k == 0) {
                     pv = a.anchor[b];
                 } else {
-                    const unsigned long long wv = __hip_atomic_load(a.winners + ((size_t)(k - 1) * a.Bpad + b) * kWinnerStride,
-                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned long long wv = pick_word(a, k - 1, b);
                     pv = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
                     pv = min(max(pv, 0), a.V - 1);
                 }
@@ -665,7 +702,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             if (half == 0 && valid_b) {
                 const unsigned long long packed =
                     ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
-                atomicMax(a.winners + ((size_t)k * a.Bpad + b) * kWinnerStride, packed);
+                atomicMax(a.winners + (((size_t)k * a.Bpad + b) * kWinnerSlots + g % kWinnerSlots) * kWinnerStride, packed);
                 const size_t o = ((size_t)k * G + g) * a.Bpad + b;
                 // read by other workgroups' finalizers within this launch
                 agent_store(a.p_mc + o, mc2);
@@ -677,12 +714,15 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         if (rb == nrb - 1) {
             // this wave's picks of position k are performed once its memory operations have completed
             wait_vmcnt<0>();
+            int last_all = 0;
             if (lane == 0) {
                 const uint32_t prev = __hip_atomic_fetch_add(&stepdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 if (prev == (uint32_t)kConsumers * (uint32_t)(k + 1) - 1u)  // last consumer wave of the workgroup
-                    __hip_atomic_fetch_add(a.barrier + kCounterStride * (g % kNumCounters), 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                    last_all = arrive(a, k) ? 1 : 0;
             }
+            // the grid's last arrival writes every copy of the release word
+            if (__shfl(last_all, 0) && lane < kBarrierGroups)
+                agent_store(a.release + kCounterStride * lane, (uint32_t)(k + 1));
         }
     }
 }
