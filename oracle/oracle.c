@@ -26,7 +26,10 @@
  * Readings where the pages leave a step open (each listed with its reason in the design notes):
  *  - position 1 is conditioned on the anchor token;
  *  - ties in every argmax / top-k go to the lower vocabulary id (never the candidate slot);
- *  - sampling is Gumbel-max at temperature T: key = l/T + G(seed,b,k,v); greedy ignores T;
+ *  - sampling a restricted candidate set (the Selector, the truncated head) is Gumbel-max at temperature
+ *    T: key = l/T + G(seed,b,k,v); greedy ignores T;
+ *  - sampling the whole vocabulary is an exact draw from softmax(l/T) by a two-level exponential race
+ *    over aligned blocks of 16 ids (one race variate per block, then inverse CDF inside the winner);
  *  - the reported log-probability is log softmax(l/T)[token] over the same set the pick ranges over;
  *  - the gate multiplies the predecessor embedding: x = W1[a] (.) H(h_k).
  *
@@ -299,6 +302,68 @@ static int pick(const double* l, const int32_t* ids, int n, int mode, uint64_t s
     return best;
 }
 
+/* Draw over the whole vocabulary in sampling mode ([DSp] "DSpark vs DFlash 2": sample from the corrected
+ * logits; the pages fix the distribution, softmax(l/T), not the sampler).  A two-level exponential race:
+ * with p_v = exp(l_v/T - M), M = max l/T, the ids are grouped in aligned blocks of 16 (the last block may
+ * be short); block j has mass S_j = sum of its p_v and one race variate E_j = -ln u(seed,row,pos, 2j).  The
+ * block with the largest S_j / E_j wins (ties to the lower block); inside it the id is the first whose
+ * inclusive prefix mass exceeds u(seed,row,pos, 2j+1) * S_j.  The minimum over blocks of E_j / S_j is
+ * exponential with rate sum S and its arg-min is block j with probability S_j / sum S (independent
+ * exponentials), and the inverse CDF then takes v with probability p_v / S_j: the draw is exactly
+ * softmax(l/T).
+ * Margin (how far the draw is from changing under small perturbations of l/T): the smaller of the top-2
+ * log race-value gap and the target's distance to the nearest interior prefix boundary of the winning
+ * block relative to its mass; a relative change eps of the masses moves both by about eps.
+ * Returns the id; writes margin, the log-softmax of l/T at the id and the log-sum-exp. */
+static int draw_blocks(const double* l, int V, uint64_t seed, int row, int pos, double T, double* margin,
+                       double* logprob, double* lse_out) {
+    double M = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if (l[v] / T > M) M = l[v] / T;
+    const int nb = (V + 15) / 16;
+    double total = 0.0, k1 = -INFINITY, k2 = -INFINITY;
+    int J = -1;
+    for (int j = 0; j < nb; ++j) {
+        const int v1 = (16 * j + 16 < V) ? 16 * j + 16 : V;
+        double S = 0.0;
+        for (int v = 16 * j; v < v1; ++v) S += exp(l[v] / T - M);
+        total += S;
+        if (!(S > 0.0)) continue;
+        const double u1 = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * j));
+        const double key = log(S) - log(-log(u1));
+        if (J < 0 || key > k1) {
+            k2 = k1;
+            k1 = key;
+            J = j;
+        } else if (key > k2) {
+            k2 = key;
+        }
+    }
+    const int v0 = 16 * J, v1 = (v0 + 16 < V) ? v0 + 16 : V;
+    double SJ = 0.0;
+    for (int v = v0; v < v1; ++v) SJ += exp(l[v] / T - M);
+    const double target = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * J + 1)) * SJ;
+    int tok = -1;
+    double cum = 0.0, dist = INFINITY;
+    for (int v = v0; v < v1; ++v) {
+        const double pv = exp(l[v] / T - M);
+        cum += pv;
+        if (tok < 0 && cum > target) tok = v;
+        if (v + 1 < v1) {  /* interior boundary after id v */
+            const double d = fabs(target - cum) / SJ;
+            if (d < dist) dist = d;
+        }
+    }
+    if (tok < 0) /* the target sits at the block's mass: the last id with mass */
+        for (int v = v1 - 1; v >= v0 && tok < 0; --v)
+            if (exp(l[v] / T - M) > 0.0) tok = v;
+    const double lse = M + log(total);
+    if (margin) *margin = (k1 - k2 < dist) ? k1 - k2 : dist;
+    if (logprob) *logprob = l[tok] / T - lse;
+    if (lse_out) *lse_out = lse;
+    return tok;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* O-M: full-vocabulary Markov head, K serial positions                                         */
 /* ------------------------------------------------------------------------------------------ */
@@ -311,7 +376,8 @@ static int pick(const double* l, const int32_t* ids, int n, int mode, uint64_t s
  * H: [B, K, r] gate values or NULL.  follow: [B, K] or NULL -- when given, the predecessor of position
  * k > 0 is follow[b, k-1] instead of the oracle's own pick (teacher forcing along a given path).
  * rows: list of nrows row ids to compute (NULL: all B rows).
- * Outputs at [b*K + k]: tokens, logprobs (log softmax at the pick), margins (top-2 key gap),
+ * Outputs at [b*K + k]: tokens, logprobs (log softmax at the pick), margins (greedy: top-2 logit gap;
+ * sampling: the race margin of draw_blocks),
  * lp_follow (log softmax at follow[b,k], or NULL), best_logit (l at the pick, or NULL). */
 void oracle_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
                          const int32_t* anchor, const double* H, int B, int K, int V, int r, int mode,
@@ -331,7 +397,8 @@ void oracle_markov_draft(const float* U, const void* W1, const void* W2, int wdt
             predecessor_embedding(W1, wdtype, r, prev, Hk, x);
             for (int v = 0; v < V; ++v) l[v] = calibrated_logit(Uk, W2, wdtype, w2_layout, V, r, x, v);
             double margin, lp, lse;
-            int tok = pick(l, NULL, V, mode, seed, b, k, temperature, &margin, &lp, &lse);
+            int tok = (mode == OR_SAMPLE) ? draw_blocks(l, V, seed, b, k, temperature, &margin, &lp, &lse)
+                                          : pick(l, NULL, V, mode, seed, b, k, temperature, &margin, &lp, &lse);
             size_t o = (size_t)b * K + k;
             tokens[o] = tok;
             if (logprobs) logprobs[o] = lp;

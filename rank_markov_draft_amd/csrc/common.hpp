@@ -44,25 +44,42 @@ __device__ __forceinline__ uint32_t noise_key2(uint32_t k0, uint32_t b, uint32_t
     return fmix32(fmix32(k0 ^ b) ^ k);
 }
 
-// -log2(-ln u) + log2(ln 2) = -log2(-log2 u), i.e. the Gumbel variate G(u) = -ln(-ln u) times log2(e) up to
-// the constant -log2(ln 2), for the uniform u = (2 * (h >> 9) + 1) / 2^24 of hash h.  Only differences of
-// this value enter an argmax, so the constant is dropped.
-//
-// u is formed exactly: 1 + m 2^-23 (m = h >> 9) minus (1 - 2^-24) has no rounding error.  For u close to 1
-// the hardware log2 is replaced by the series -ln(1 - w) = w + w^2/2 + w^3/3 + w^4/4 with w = 1 - u
-// (exact), whose truncation error is below 2^-26 relative for w < 2^-7.
-__device__ __forceinline__ float gumbel_log2_units(uint32_t h) {
+// Uniform u = (2 (h >> 9) + 1) / 2^24 of hash h, in (0, 1).  Formed exactly: 1 + m 2^-23 (m = h >> 9) minus
+// (1 - 2^-24) has no rounding error.
+__device__ __forceinline__ float hash_uniform(uint32_t h) {
+    return __uint_as_float((h >> 9) | 0x3F800000u) - 0.99999994039535522f;
+}
+
+// -log2 u > 0 for that uniform.  Close to u = 1 the hardware log2 is replaced by the series
+// -ln(1 - w) = w + w^2/2 + w^3/3 + w^4/4 with w = 1 - u (exact), whose truncation error is below 2^-26
+// relative for w < 2^-7.
+__device__ __forceinline__ float neg_log2_uniform(uint32_t h) {
     const uint32_t m = h >> 9;
     const float u = __uint_as_float(m | 0x3F800000u) - 0.99999994039535522f;
     const float w = (float)(2u * (0x7FFFFFu - m) + 1u) * 5.9604644775390625e-8f;  // 1 - u, exact
-    float e2;  // -log2(u) > 0
-    if (w < 0.0078125f) {
-        e2 = w * (1.0f + w * (0.5f + w * (0.33333334f + w * 0.25f))) * kLog2e;
-    } else {
-        e2 = -__builtin_amdgcn_logf(u);
-    }
-    return -__builtin_amdgcn_logf(e2);
+    const float series = w * (1.0f + w * (0.5f + w * (0.33333334f + w * 0.25f))) * kLog2e;
+    return (w < 0.0078125f) ? series : -__builtin_amdgcn_logf(u);
 }
+
+// -log2(-ln u) + log2(ln 2) = -log2(-log2 u), i.e. the Gumbel variate G(u) = -ln(-ln u) times log2(e) up to
+// the constant -log2(ln 2), for the uniform of hash h.  Only differences of this value enter an argmax, so
+// the constant is dropped.  (Gumbel-max over a restricted candidate set.)
+__device__ __forceinline__ float gumbel_log2_units(uint32_t h) { return -__builtin_amdgcn_logf(neg_log2_uniform(h)); }
+
+// Whole-vocabulary draw, block q (ids 16 q .. 16 q + 15) of a two-level exponential race: its race variate
+// E = -log2 u(2 q) and its inverse-CDF target u(2 q + 1) sb for block mass sb > 0, kept strictly below sb;
+// u(n) is the uniform of fmix32(k2 ^ n).  The block with the largest sb / E wins; inside it the drawn id is
+// the first whose inclusive prefix mass (slot order) exceeds the target.
+__device__ __forceinline__ void block_race_variates(uint32_t k2, uint32_t q, float sb, float& E, float& target) {
+    E = neg_log2_uniform(fmix32(k2 ^ (2u * q)));
+    const float u2 = hash_uniform(fmix32(k2 ^ (2u * q + 1u)));
+    target = fminf(u2 * sb, __uint_as_float(__float_as_uint(sb) - 1u));
+}
+
+// Row rho of a staged 32-row W2 tile (vocabulary id v0 + rho) goes to LDS slot w2_slot(rho).  A 32x32x16 MFMA's
+// A-operand row m (read by lanes m and m + 32) produces accumulator rows 8 (i / 4) + 4 (lane / 32) + i % 4, so
+// with this order accumulator i of a lane holds id v0 + 16 (lane / 32) + i: 16 consecutive ids per lane.
+__device__ __forceinline__ int w2_slot(int rho) { return 8 * ((rho & 15) >> 2) + 4 * (rho >> 4) + (rho & 3); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

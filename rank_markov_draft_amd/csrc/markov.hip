@@ -59,17 +59,18 @@ __device__ __forceinline__ void store_w2_tile(uint8_t* lds, const u32x4_t (&reg)
         int c = threadIdx.x + q * kThreads;
         if (c < G::kChunks) {
             int row = c / (2 * RK), ch = c % (2 * RK);
-            *reinterpret_cast<u32x4_t*>(lds + row * G::kStride + ch * 16) = reg[q];
+            *reinterpret_cast<u32x4_t*>(lds + w2_slot(row) * G::kStride + ch * 16) = reg[q];
         }
     }
 }
 
-// U_k values of this lane's row for the 16 accumulator slots of tile v0: slot i <-> v0 + 8*(i/4) + 4*half + i%4.
+// U_k values of this lane's row for the 16 accumulator slots of tile v0: slot i <-> v0 + 16*half + i (the W2
+// tile is staged in w2_slot order).
 template <bool VEC>
 __device__ __forceinline__ void load_u_tile(const float* __restrict__ urow, bool valid_b, int V, int v0, int half, float (&u)[16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        int v = v0 + 8 * q + 4 * half;
+        int v = v0 + 16 * half + 4 * q;
         if (VEC) {
             f32x4_t x = {0.f, 0.f, 0.f, 0.f};
             if (valid_b && v < V) x = load_nt_f32x4(urow + v);
@@ -141,6 +142,9 @@ __global__ void __launch_bounds__(kThreads, 2) markov_step_mfma(StepArgs a) {
 
     float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
     int bi = 0x7FFFFFFF;
+    // sampling (two-level exponential race over the lane's aligned 16-id blocks): mass of the best block so
+    // far and of the id drawn in it (scaled as s), and the block's race variate
+    float bs = 0.f, bE = 1.f, be = 0.f;
 
     if (tile_begin < tile_end) store_w2_tile<RK>(lds[0], wreg);
     __syncthreads();
@@ -168,7 +172,7 @@ __global__ void __launch_bounds__(kThreads, 2) markov_step_mfma(StepArgs a) {
             // validation epilogue: write the calibrated logits
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int v = v0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const int v = v0 + 16 * half + i;
                 if (valid_b && v < a.V) a.logits_out[(size_t)b * a.V + v] = acc[i] + ucur[i];
             }
         } else {
@@ -177,30 +181,56 @@ __global__ void __launch_bounds__(kThreads, 2) markov_step_mfma(StepArgs a) {
             float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int v = v0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const int v = v0 + 16 * half + i;
                 const bool ok = valid_b && v < a.V;
                 lv[i] = acc[i] + ucur[i];
                 tv[i] = ok ? lv[i] * a.c : -INFINITY;
                 tmax = fmaxf(tmax, tv[i]);
             }
             const float mn = fmaxf(m, tmax);
-            s *= fast_exp2(m - mn);
+            const float scale = fast_exp2(m - mn);
+            s *= scale;
             m = mn;
+            if (SAMPLE) {
+                // the lane's 16 ids are the aligned block q = v0 / 16 + half: its mass, race and drawn id
+                bs *= scale;
+                be *= scale;
+                float e[16], sb = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s += fast_exp2(tv[i] - m);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int v = v0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                float key;
-                if (SAMPLE) {
-                    key = tv[i] + gumbel_log2_units(fmix32(k2 ^ (uint32_t)v));
-                } else {
-                    key = (valid_b && v < a.V) ? lv[i] : -INFINITY;
+                for (int i = 0; i < 16; ++i) {
+                    e[i] = fast_exp2(tv[i] - m);
+                    sb += e[i];
                 }
-                if (key > bk) {
-                    bk = key;
-                    bi = v;
-                    bl = lv[i];
+                s += sb;
+                float E, target;
+                block_race_variates(k2, (uint32_t)(v0 / 16 + half), sb, E, target);
+                float cum = 0.f, esel = e[0];
+                int sel = 0;
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+                    cum += e[i];
+                    const bool below = cum <= target;
+                    sel += below ? 1 : 0;
+                    esel = below ? e[i + 1] : esel;
+                }
+                if (sb * bE > bs * E) {
+                    bs = sb;
+                    bE = E;
+                    be = esel;
+                    bi = v0 + 16 * half + sel;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s += fast_exp2(tv[i] - m);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int v = v0 + 16 * half + i;
+                    const float key = (valid_b && v < a.V) ? lv[i] : -INFINITY;
+                    if (key > bk) {
+                        bk = key;
+                        bi = v;
+                        bl = lv[i];
+                    }
                 }
             }
         }
@@ -210,6 +240,11 @@ __global__ void __launch_bounds__(kThreads, 2) markov_step_mfma(StepArgs a) {
     }
 
     if (STORE) return;
+    if (SAMPLE && bs > 0.f) {
+        // race key log2(S / E) with S in absolute units; the drawn id's logit from its mass
+        bk = fast_log2(bs) + m - fast_log2(bE);
+        bl = (fast_log2(be) + m) / a.c;
+    }
     // lanes l and l + 32 hold the same row
     {
         float ok_ = __shfl_xor(bk, 32);
@@ -281,29 +316,62 @@ __global__ void __launch_bounds__(kThreads) markov_step_valu(StepArgsValu a) {
         bi[rb] = 0x7FFFFFFF;
         k2[rb] = SAMPLE ? noise_key2(a.k0, (uint32_t)(blockIdx.y * kValuRows + rb), (uint32_t)a.k) : 0u;
     }
-    for (int v = blockIdx.x * kThreads + threadIdx.x; v < a.V; v += gridDim.x * kThreads) {
+    // Every thread of the workgroup runs the same iterations (the sampling race works on groups of 16 lanes):
+    // thread t takes id v0 + t of each 256-id span.
+    const int g16 = threadIdx.x & 15;
+    for (int v0 = blockIdx.x * kThreads; v0 < a.V; v0 += gridDim.x * kThreads) {
+        const int v = v0 + threadIdx.x;
+        const bool inr = v < a.V;
         float acc[kValuRows] = {};
-        for (int j = 0; j < r; ++j) {
-            const float w = wload<WT>(W2, (size_t)j * a.sj + (size_t)v * a.sv);
+        if (inr) {
+            for (int j = 0; j < r; ++j) {
+                const float w = wload<WT>(W2, (size_t)j * a.sj + (size_t)v * a.sv);
 #pragma unroll
-            for (int rb = 0; rb < kValuRows; ++rb) acc[rb] = fmaf(xs[rb * r + j], w, acc[rb]);
+                for (int rb = 0; rb < kValuRows; ++rb) acc[rb] = fmaf(xs[rb * r + j], w, acc[rb]);
+            }
         }
 #pragma unroll
         for (int rb = 0; rb < kValuRows; ++rb) {
             const int b = blockIdx.y * kValuRows + rb;
-            if (b >= a.B) continue;
-            const float l = acc[rb] + a.U[(size_t)b * a.u_stride + v];
+            if (b >= a.B) continue;  // uniform over the workgroup
+            const float l = inr ? acc[rb] + a.U[(size_t)b * a.u_stride + v] : 0.f;
             if (STORE) {
-                a.logits_out[(size_t)b * a.V + v] = l;
+                if (inr) a.logits_out[(size_t)b * a.V + v] = l;
                 continue;
             }
-            const float t = l * a.c;
+            const float t = inr ? l * a.c : -INFINITY;
             const float mn = fmaxf(m[rb], t);
             s[rb] = s[rb] * fast_exp2(m[rb] - mn) + fast_exp2(t - mn);
             m[rb] = mn;
-            const float key = SAMPLE ? t + gumbel_log2_units(fmix32(k2[rb] ^ (uint32_t)v)) : l;
-            if (key > bk[rb]) {
-                bk[rb] = key;
+            if (SAMPLE) {
+                // Whole-vocabulary draw, block of ids v - g16 .. v - g16 + 15 (16 lanes): block max, masses,
+                // inclusive prefix masses in id order, the race variate and the inverse-CDF draw.
+                float M = t;
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+                const float e = inr ? fast_exp2(t - M) : 0.f;
+                float P = e;
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    const float y = __shfl_up(P, off, 16);
+                    if (g16 >= off) P += y;
+                }
+                const float S = __shfl(P, 15, 16);
+                if (S > 0.f) {
+                    float E, target;
+                    block_race_variates(k2[rb], (uint32_t)((v - g16) / 16), S, E, target);
+                    const unsigned long long below = __ballot(P <= target && g16 < 15);
+                    const int sel = __popcll((below >> (threadIdx.x & 48)) & 0x7FFFull);
+                    const float key = fast_log2(S) + M - fast_log2(E);
+                    const float lsel = __shfl(l, sel, 16);
+                    if (key > bk[rb]) {
+                        bk[rb] = key;
+                        bi[rb] = v - g16 + sel;
+                        bl[rb] = lsel;
+                    }
+                }
+            } else if (inr && l > bk[rb]) {
+                bk[rb] = l;
                 bi[rb] = v;
                 bl[rb] = l;
             }

@@ -21,8 +21,10 @@
 //    position; C seeded with the U tile).  A lane holds one batch row and 16 consecutive vocabulary ids of
 //    the accumulator; calibration, the streaming log-sum-exp and the running pick are per-lane scalars.  The
 //    MFMAs of tile t + 1 are issued inside the epilogue of tile t.  No logits are written.
-//  * Sampling uses the exponential-race form of Gumbel-max: argmax_v p_v / E_v with p_v = 2^(l_v c - m) (the
-//    same exponential the log-sum-exp needs) and E_v = -log2 u_v, which is argmax_v (l_v / T + G_v) exactly.
+//  * Sampling is an exact draw from softmax(l / T) by a two-level exponential race: a lane's 16 ids of a tile
+//    form one aligned block whose mass S = sum_v 2^(l_v c - m) (the same exponentials the log-sum-exp needs)
+//    races with one exponential variate, and the winning block's id is drawn by inverse CDF, so one hash
+//    pair and one logarithm serve 16 ids.
 //  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id), spread over two
 //    words per row, gives the global pick with ties to the lower id; log-sum-exp partials go to the
 //    workspace.  A grid barrier then releases the next position, whose workgroups gather W1 rows of the new
@@ -59,11 +61,6 @@ struct Ring {
     static constexpr int kUnitsPerProducer = (kUnits + 3) / 4;
     static constexpr int kDepth = 3;                        // items in flight per producer, in registers
 };
-
-// Row rho of a W2 tile (vocabulary id v0 + rho) is stored in LDS slot w2_slot(rho).  MFMA A-operand row m
-// (read by lanes m and m + 32) produces accumulator rows 8 (i / 4) + 4 (lane / 32) + i % 4, so with this
-// order accumulator i of a lane holds id v0 + 16 (lane / 32) + i: 16 consecutive ids per lane.
-__device__ __forceinline__ int w2_slot(int rho) { return 8 * ((rho & 15) >> 2) + 4 * (rho >> 4) + (rho & 3); }
 
 constexpr int kGateItems = 4;  // items of the next position that may be in flight at a position boundary
 constexpr int kConsumers = 4;
@@ -424,7 +421,9 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     bf16x8_t xf[RK];
     uint32_t k2 = 0;
     float m = kNegBig, s = 0.f;  // running max of l (natural units) and sum of 2^(l c - m c)
-    float bp = 0.f, bE = 1.f;    // sampling: best p = 2^(l c - m c) and its E = -log2 u
+    // sampling: mass of the lane's best block so far (scaled as s), its race variate E = -log2 u, and the mass
+    // of the id drawn inside it
+    float bs = 0.f, bE = 1.f, be = 0.f;
     float bl = -INFINITY;        // greedy: best logit
     int bslot = 0, btile = -1;   // best id = 32 btile + 16 half + bslot
     const float c = a.c;
@@ -479,7 +478,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         const float mn = fmaxf(m, cm);
         const float scale = fast_exp2((m - mn) * c);
         s *= scale;
-        if (SAMPLE) bp *= scale;
+        if (SAMPLE) {
+            bs *= scale;
+            be *= scale;
+        }
         m = mn;
         mc = mn * c;
         return cm;
@@ -496,39 +498,49 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             btile = t;
         }
     };
-    // Per element j of the tile: exponential of the log-sum-exp and, for sampling, the noise and the race.
-    // Noise: fmix32(k2 ^ v) with v = y0 + j, y0 = 32 t + 16 half a multiple of 16, so k2 ^ v = (k2 ^ y0) ^ j
-    // and the first xor-shift of fmix32 is shared by the 16 ids: yb = kb ^ (kb >> 16), kb = k2 ^ y0.
-    auto tile_elem = [&](const f32x16_t& lv, int j, float mc, uint32_t yb, bool& improved) {
-        const float e = fast_exp2(fmaf(lv[j], c, -mc));
-        s += e;
-        if (SAMPLE) {
-            uint32_t h = (yb ^ (uint32_t)j) * 0x85EBCA6Bu;
-            h ^= h >> 13;
-            h *= 0xC2B2AE35u;
-            h ^= h >> 16;
-            const float uu = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, h, 9)) - 0.99999994039535522f;
-            const float E = -fast_log2(uu);  // -log2 u > 0
-            // exponential race: p / E > bp / bE  <=>  l c - log2 E beats the best so far
-            const bool better = e * bE > bp * E;
-            bp = better ? e : bp;
-            bE = better ? E : bE;
-            bslot = better ? j : bslot;
-            improved |= better;
-        }
+    auto greedy_elem = [&](const f32x16_t& lv, int j, float mc) { s += fast_exp2(fmaf(lv[j], c, -mc)); };
+
+    // Sampling draws over the whole vocabulary with a two-level exponential race.  A lane's 16 ids of a tile
+    // are one aligned block (ids 16 q .. 16 q + 15, q = 2 t + half).  The block's mass S = sum_v 2^(l_v c - m c)
+    // races with one variate E = -log2 u(2 q): the block with the largest S / E wins, and inside the winner the
+    // id is drawn by inverse CDF with target u(2 q + 1) S, where u(n) is the uniform of hash fmix32(k2 ^ n).
+    // The winner is distributed as S / sum S (independent exponential clocks) and the id inside as its share
+    // of S, so the draw is exactly softmax(l / T): one hash pair and one logarithm per 16 ids.
+    // Pass 1, element j: its mass replaces the logit in lv, and sb accumulates the block mass in slot order.
+    auto sample_mass = [&](f32x16_t& lv, int j, float mc, float& sb) {
+        lv[j] = fast_exp2(fmaf(lv[j], c, -mc));
+        sb += lv[j];
     };
-    auto noise_base = [&](int t) -> uint32_t {
-        const uint32_t kb = k2 ^ (uint32_t)(t * kRTileV + 16 * half);
-        return kb ^ (kb >> 16);
+    // The block's race variate and the inverse-CDF target, which stays strictly below the block mass.
+    auto sample_block = [&](int t, float sb, float& E, float& target) {
+        block_race_variates(k2, 2u * (uint32_t)t + (uint32_t)half, sb, E, target);
     };
+    // Pass 2, element j < 15: the drawn slot is the number of inclusive prefixes (same order as sb) at or
+    // below the target; esel follows the mass of that slot.
+    auto sample_cdf = [&](const f32x16_t& lv, int j, float target, float& cum, int& sel, float& esel) {
+        cum += lv[j];
+        const bool below = cum <= target;
+        sel += below ? 1 : 0;
+        esel = below ? lv[j + 1] : esel;
+    };
+    // The race against the lane's best block: S / E > bs / bE.
+    auto sample_update = [&](int t, float sb, float E, int sel, float esel) {
+        const bool better = sb * bE > bs * E;
+        bs = better ? sb : bs;
+        bE = better ? E : bE;
+        be = better ? esel : be;
+        bslot = better ? sel : bslot;
+        btile = better ? t : btile;
+    };
+
     // Tile tt's epilogue in one straight-line block with the operand reads and the MFMAs of tile tt + 1 (into
     // nxt), so the matrix cores' dependent accumulation chain runs under the vector ALUs' work.
     auto pipelined = [&](f32x16_t& cur, f32x16_t& nxt, int i, int t) {
         const std::integral_constant<bool, false> kUnmasked{};
         // The next tile's reads first (its U tile and the first two A operands), then the head of this tile's
-        // epilogue while they land.  Then, per element, the A operand two MFMAs ahead, one MFMA and the
-        // element's vector work.  The scheduling barriers keep that order: left alone, the scheduler reads each
-        // A operand right before its MFMA and stalls the wave on every read.
+        // epilogue while they land.  Then 16 steps, each: the A operand two MFMAs ahead, one MFMA and a share
+        // of the epilogue's vector work.  The scheduling barriers keep that order: left alone, the scheduler
+        // reads each A operand right before its MFMA and stalls the wave on every read.
         nxt = read_u(i + 1);
         bf16x8_t fr[RK];
         fr[0] = frag(i + 1, 0);
@@ -536,27 +548,53 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         if (SAMPLE) __builtin_amdgcn_sched_barrier(0);
         float mc;
         const float cm = tile_head(cur, t, kUnmasked, mc);
-        const uint32_t yb = SAMPLE ? noise_base(t) : 0u;
-        bool improved = false;
+        float sb = 0.f, E = 1.f, target = 0.f, cum = 0.f, esel = 0.f;
+        int sel = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             if (j + 2 < RK) fr[j + 2] = frag(i + 1, j + 2);
             if (j < RK) nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], xf[j], nxt, 0, 0, 0);
-            tile_elem(cur, j, mc, yb, improved);
-            if (SAMPLE) __builtin_amdgcn_sched_barrier(0);
+            if (SAMPLE) {
+                // steps 0-7: masses of slots 2j, 2j+1; step 8: the block's variates; steps 8-15: inverse CDF
+                if (j < 8) {
+                    sample_mass(cur, 2 * j, mc, sb);
+                    sample_mass(cur, 2 * j + 1, mc, sb);
+                } else {
+                    if (j == 8) {
+                        s += sb;
+                        sample_block(t, sb, E, target);
+                        esel = cur[0];
+                    }
+                    sample_cdf(cur, 2 * (j - 8), target, cum, sel, esel);
+                    if (j < 15) sample_cdf(cur, 2 * (j - 8) + 1, target, cum, sel, esel);
+                    else sample_update(t, sb, E, sel, esel);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                greedy_elem(cur, j, mc);
+            }
         }
-        if (SAMPLE) btile = improved ? t : btile;
-        else greedy_pick(cur, cm, t);
+        if (!SAMPLE) greedy_pick(cur, cm, t);
     };
     auto last = [&](f32x16_t& cur, int t, auto mask_tail) {
         float mc;
         const float cm = tile_head(cur, t, mask_tail, mc);
-        const uint32_t yb = SAMPLE ? noise_base(t) : 0u;
-        bool improved = false;
+        if (SAMPLE) {
+            float sb = 0.f, E, target, cum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) tile_elem(cur, j, mc, yb, improved);
-        if (SAMPLE) btile = improved ? t : btile;
-        else greedy_pick(cur, cm, t);
+            for (int j = 0; j < 16; ++j) sample_mass(cur, j, mc, sb);
+            s += sb;
+            sample_block(t, sb, E, target);
+            float esel = cur[0];
+            int sel = 0;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) sample_cdf(cur, j, target, cum, sel, esel);
+            sample_update(t, sb, E, sel, esel);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) greedy_elem(cur, j, mc);
+            greedy_pick(cur, cm, t);
+        }
     };
 
     const int nseg = a.K * nrb;
@@ -629,8 +667,9 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         }
         m = kNegBig;
         s = 0.f;
-        bp = 0.f;
+        bs = 0.f;
         bE = 1.f;
+        be = 0.f;
         bl = -INFINITY;
         bslot = 0;
         btile = -1;
@@ -677,9 +716,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             int bi = (btile >= 0) ? 32 * btile + 16 * half + bslot : 0x7FFFFFFF;
             float key, lbest;
             if (SAMPLE) {
-                const float lc = fast_log2(bp) + m * c;  // l_best * c
-                key = (bp > 0.f) ? lc - fast_log2(bE) : -INFINITY;
-                lbest = lc / c;
+                // race key log2(S / E) with S in absolute units, and the logit of the drawn id from its mass
+                const float mcb = m * c;
+                key = (bs > 0.f) ? fast_log2(bs) + mcb - fast_log2(bE) : -INFINITY;
+                lbest = (fast_log2(be) + mcb) / c;
             } else {
                 key = bl;
                 lbest = bl;

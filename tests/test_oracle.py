@@ -149,21 +149,69 @@ def test_w2_zero_greedy_is_per_position_argmax():
 
 
 @pytest.mark.parametrize("T", [1.0, 0.7])
-def test_w2_zero_sample_is_gumbel_max_of_U(T):
+def test_whole_vocabulary_draw_follows_softmax(T):
+    """Statistics: with W2 = 0 the logits are U, so a whole-vocabulary draw must follow softmax(U/T).
+    V = 40 spans three blocks of the race (16, 16 and a short one of 8); one row replicated over 2^16
+    rows (the noise keys on the row) gives independent draws, compared by chi-square.  A wrong race
+    value (block mass without its variate, or the variate without the mass), a wrong block grouping or a
+    reversed inverse CDF each fail.  The reported log-probability is the exact log-softmax."""
     rng = np.random.default_rng(5)
-    B, K, V, r = 4, 3, 64, 8
-    U = rng.standard_normal((B, K, V)).astype(np.float32)
+    V, r, n = 40, 8, 1 << 16
+    u = (rng.standard_normal(V) * 1.3).astype(np.float32)
+    U = np.broadcast_to(u, (n, 1, V)).copy()
     W1 = rng.standard_normal((V, r)).astype(np.float32)
     W2 = np.zeros((r, V), np.float32)
-    anchor = rng.integers(0, V, B).astype(np.int32)
+    anchor = np.zeros(n, np.int32)
     res = O.markov_draft(U, W1, W2, anchor, mode=O.SAMPLE, seed=99, temperature=T)
+    p = special.softmax(u.astype(np.float64) / T)
+    counts = np.bincount(res["tokens"][:, 0], minlength=V)
+    expect = p * n
+    keep = expect > 5
+    chi2 = ((counts[keep] - expect[keep]) ** 2 / expect[keep]).sum()
+    assert stats.chi2.sf(chi2, keep.sum() - 1) > 1e-4
+    lp = np.log(p)
+    np.testing.assert_allclose(res["logprobs"][:, 0], lp[res["tokens"][:, 0]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("V", [1, 7, 16])
+def test_single_block_draw_is_inverse_transform_sampling(V):
+    """Special case: with V <= 16 the race has one block, and the draw reduces to inverse transform
+    sampling of softmax(l/T) with the uniform of noise id 1: numpy's searchsorted over the cumulative
+    masses (first id whose inclusive prefix exceeds u times the total)."""
+    rng = np.random.default_rng(40 + V)
+    B, K, r, T = 64, 3, 4, 0.8
+    U = (rng.standard_normal((B, K, V)) * 2).astype(np.float32)
+    W1 = np.zeros((V, r), np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    res = O.markov_draft(U, W1, W2, np.zeros(B, np.int32), mode=O.SAMPLE, seed=3, temperature=T)
     for b in range(B):
         for k in range(K):
-            _, g = O.noise_fill(99, b, k, 0, V)
-            key = U[b, k].astype(np.float64) / T + g
-            assert res["tokens"][b, k] == int(np.argmax(key))
-            lp = U[b, k].astype(np.float64) / T - special.logsumexp(U[b, k].astype(np.float64) / T)
-            assert abs(res["logprobs"][b, k] - lp[res["tokens"][b, k]]) < 1e-12
+            z = U[b, k].astype(np.float64) / T
+            w = np.exp(z - z.max())
+            cum = np.cumsum(w)
+            tok = int(np.searchsorted(cum, O.noise_uniform(3, b, k, 1) * cum[-1], side="right"))
+            assert res["tokens"][b, k] == min(tok, V - 1)
+
+
+def test_two_point_race_is_the_exponential_race():
+    """Special case: two blocks, each with its mass on one id (ids 3 and 20, logits a and b; every other
+    logit is -1e30).  The draw is then the plain exponential race of two clocks: id 3 exactly when
+    e^a / E_0 > e^b / E_1 with E_j = -ln u(2j), and id 3 has probability e^a / (e^a + e^b)."""
+    rng = np.random.default_rng(17)
+    n, V, r = 1 << 14, 32, 4
+    a, b = 0.4, -0.3
+    U = np.full((n, 1, V), -1e30, np.float32)
+    U[:, 0, 3] = a
+    U[:, 0, 20] = b
+    res = O.markov_draft(U, np.zeros((V, r), np.float32), np.zeros((r, V), np.float32), np.zeros(n, np.int32),
+                         mode=O.SAMPLE, seed=11)
+    for row in rng.integers(0, n, 200):
+        e0 = -math.log(O.noise_uniform(11, int(row), 0, 0))
+        e1 = -math.log(O.noise_uniform(11, int(row), 0, 2))
+        assert res["tokens"][row, 0] == (3 if math.exp(a) / e0 > math.exp(b) / e1 else 20)
+    frac = float(np.mean(res["tokens"][:, 0] == 3))
+    pa = math.exp(a) / (math.exp(a) + math.exp(b))
+    assert abs(frac - pa) < 5 * math.sqrt(pa * (1 - pa) / n)
 
 
 def _strong_tiny(V=5, K=3, r=4, seed=6, gated=False):
@@ -365,10 +413,11 @@ def test_selector_equals_markov_restricted_to_its_candidates(mode, gated):
     assert np.all(np.isin(sel["tokens"], cand.reshape(B, -1)))
 
 
-@pytest.mark.parametrize("mode", [O.GREEDY, O.SAMPLE])
+@pytest.mark.parametrize("mode", [O.GREEDY])
 def test_selector_with_topk_V_is_the_full_head(mode):
-    """Special case: with the candidate set equal to the whole vocabulary the truncation is exact,
-    in sampling too because the noise keys on the vocabulary id, not the candidate slot."""
+    """Special case: with the candidate set equal to the whole vocabulary the truncation is exact.
+    (Greedy only: a candidate set is sampled by Gumbel-max per candidate, the whole vocabulary by the
+    block race; both draw from the same softmax, with different noise.)"""
     w = S.workload("tiny", V=64)
     sel = O.selector_draft(w.U, w.W1, np.ascontiguousarray(w.W2.T), w.anchor, topk=w.V, mode=mode, seed=5)
     full = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=5)
@@ -429,10 +478,12 @@ def test_rows_are_independent_and_restricted_full_sets_is_full():
     one = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=7, rows=[2])
     assert np.array_equal(one["tokens"][2], full["tokens"][2])
     assert np.all(one["tokens"][[0, 1, 3]] == -1)
+    # greedy: the head restricted to the whole vocabulary is the head
+    fullg = O.markov_draft(w.U, w.W1, w.W2, w.anchor)
     cand = np.broadcast_to(np.arange(w.V, dtype=np.int32), (w.B, w.K, w.V))
-    res = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand, mode=O.SAMPLE, seed=7)
-    assert np.array_equal(res["tokens"], full["tokens"])
-    np.testing.assert_allclose(res["logprobs"], full["logprobs"], rtol=0, atol=1e-12)
+    res = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand)
+    assert np.array_equal(res["tokens"], fullg["tokens"])
+    np.testing.assert_allclose(res["logprobs"], fullg["logprobs"], rtol=0, atol=1e-12)
 
 
 def test_shift_invariance():
