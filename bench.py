@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
 
 A step is one draft round of the serving workload: B=128 rows, K=16 positions, vocabulary V=151936, rank
-r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, Gumbel-max sampling at T=1 with
+r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, sampling at T=1 (block-race draw from softmax) with
 log-probabilities, i.e. dspark_markov_draft: for every position the fused bias-contraction / calibration
 / pick kernel and the cross-workgroup reduction.  Inputs are synthetic (the seeded generator) and are
 resident in HBM before timing starts.  Before every timed round a 1 GiB fill evicts the L2 and the
@@ -392,14 +392,14 @@ def main():
         O.markov_draft(w.U, w.W1, W2Th, w.anchor, w2_layout=O.W2_VR, mode=O.SAMPLE, seed=w.noise_seed, rows=rows)
         dt = time.perf_counter() - t0
         cpu = {"value": round(nrows * w.K / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"serving workload rows 0..{nrows - 1} of {w.B}, all {w.K} positions, Gumbel-max T=1 "
+               "sample": f"serving workload rows 0..{nrows - 1} of {w.B}, all {w.K} positions, sampling T=1 "
                          f"({nrows * w.K} draft tokens, fp64, {dt:.1f} s)"}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "pct_of_roofline": extras["pct_of_hbm_roofline"], "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "serving: Markov-head draft round, Gumbel-max T=1, with log-probabilities",
+        "config": {"workload": "serving: Markov-head draft round, sampling T=1, with log-probabilities",
                    "B": B, "K": K, "V": V, "r": r, "weights": "bf16 (W2 stored [V, r])", "base_logits": "fp32",
                    "accumulate": "fp32", "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "extras": extras,

@@ -30,15 +30,20 @@
  *    last non-OK status.  No C++ exception crosses this boundary.
  *  - Preconditions not checked on the host: token ids (anchor, prev) lie in [0, V); U, H and the
  *    weights are finite.  Violations give unspecified results.
- *  - Token ties: every argmax, Gumbel-max, top-k and walk breaks ties towards the lower vocabulary id.
+ *  - Token ties: every argmax, race, top-k and walk breaks ties towards the lower vocabulary id.
  *  - Determinism: identical inputs, seed and shapes give bit-identical outputs on one device.
  *  - Calls on one stream run in order; concurrent calls need distinct workspaces.
  *
- * Noise (sampling mode).  The pages fix no generator.  Gumbel noise G(seed, b, k, v) is derived from a
- * counter hash: fmix(x) is the MurmurHash3 32-bit finalisation mix (A. Appleby, public domain);
- * k0 = fmix(lo32(seed) ^ fmix(hi32(seed))), k1 = fmix(k0 ^ b), k2 = fmix(k1 ^ k), h = fmix(k2 ^ v);
- * u = (2 * (h >> 9) + 1) / 2^24; G = -ln(-ln u).  b is the batch row, k the draft position (0-based),
- * v the vocabulary id (never a candidate slot).  The pick is argmax_v of l_v / T + G(seed, b, k, v).
+ * Noise (sampling mode).  The pages fix the distribution (softmax(l / T)), not the generator.  Uniforms come
+ * from a counter hash: fmix(x) is the MurmurHash3 32-bit finalisation mix (A. Appleby, public domain);
+ * k0 = fmix(lo32(seed) ^ fmix(hi32(seed))), k1 = fmix(k0 ^ b), k2 = fmix(k1 ^ k), h(n) = fmix(k2 ^ n);
+ * u(n) = (2 * (h(n) >> 9) + 1) / 2^24.  b is the batch row, k the draft position (0-based).
+ *  - Whole-vocabulary draws (the Markov head) race aligned blocks of 16 ids: with p_v = exp(l_v / T - M),
+ *    block j (ids 16 j .. 16 j + 15) has mass S_j = sum of its p_v and variate E_j = -ln u(2 j); the block
+ *    with the largest S_j / E_j wins, and the drawn id is the first in it whose inclusive prefix mass
+ *    exceeds u(2 j + 1) S_j.  An exact draw from softmax(l / T).
+ *  - Restricted candidate sets (the Selector's walk) use Gumbel-max: argmax over the candidates of
+ *    l_v / T + G(v), G(v) = -ln(-ln u(v)) with n = v the vocabulary id (never a candidate slot).
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -69,7 +74,7 @@ extern "C" {
 
 /* pick rule */
 #define DSPARK_GREEDY 0 /* argmax of the calibrated logits; temperature ignored (T = 1) */
-#define DSPARK_SAMPLE 1 /* Gumbel-max at temperature T: an exact sample of softmax(l / T) */
+#define DSPARK_SAMPLE 1 /* an exact sample of softmax(l / T) at temperature T (see Noise) */
 
 /* Version of this ABI (DSPARK_ABI_VERSION of the built library). */
 int dspark_abi_version(void);
@@ -92,7 +97,7 @@ size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int
  * generation" and "The Markov head"; the equivalence page, section "What the two methods do").
  * For k = 0 .. K-1 and every row b, with a_0 = anchor[b] and a_k = tokens[b, k-1]:
  *     l[v]          = U[b, k, v] + sum_j x[j] * W2[j, v],   x = W1[a_k, :] (.) H[b, k, :]  (H == NULL: x = W1[a_k])
- *     tokens[b, k]  = argmax_v key(v),   key = l[v] (GREEDY) or l[v] / T + G(seed, b, k, v) (SAMPLE)
+ *     tokens[b, k]  = argmax_v l[v] (GREEDY) or the block-race draw from softmax(l / T) (SAMPLE; see Noise)
  *     logprobs[b,k] = l[tok] / T - log sum_v exp(l[v] / T)   (T = 1 in GREEDY)
  *
  * U        [B, K, V] fp32.
@@ -226,8 +231,8 @@ size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk);
  *  2. pair scores, all in parallel: the anchor row  S0[b, j] = U[b,0,c_0j] + < A[anchor_b] (.) H[b,0], Bemb[c_0j] >
  *     and for t >= 1  S_t[b, i, j] = U[b,t,c_tj] + < A[c_{t-1,i}] (.) H[b,t], Bemb[c_tj] >;
  *  3. the walk: i_0 = pick over S0[b, :], i_t = pick over S_t[b, i_{t-1}, :]; tokens[b, t] = c_{t, i_t}.
- *     The pick is the same GREEDY / SAMPLE rule as the Markov head over the k candidates, keyed on
- *     vocabulary ids; logprobs[b, t] = log softmax over the walked row of scores / T.
+ *     The pick over the k candidates is the argmax (GREEDY) or Gumbel-max keyed on vocabulary ids
+ *     (SAMPLE; see Noise); logprobs[b, t] = log softmax over the walked row of scores / T.
  * U [B, K, V] fp32; A, Bemb [V, r] of type wdtype; anchor [B]; H [B, K, r] fp32 or NULL.
  * topk as for dspark_topk; r <= 1024 (rows are staged with 16-byte loads when r % 8 == 0 for bf16 or
  * r % 4 == 0 for fp32 and A, Bemb are 16-byte aligned, element by element otherwise).
