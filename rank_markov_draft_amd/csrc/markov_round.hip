@@ -545,7 +545,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         bf16x8_t fr[RK];
         fr[0] = frag(i + 1, 0);
         if (RK > 1) fr[1] = frag(i + 1, 1);
-        if (SAMPLE) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         float mc;
         const float cm = tile_head(cur, t, kUnmasked, mc);
         float sb = 0.f, E = 1.f, target = 0.f, cum = 0.f, esel = 0.f;
@@ -569,10 +569,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                     if (j < 15) sample_cdf(cur, 2 * (j - 8) + 1, target, cum, sel, esel);
                     else sample_update(t, sb, E, sel, esel);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             } else {
                 greedy_elem(cur, j, mc);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (!SAMPLE) greedy_pick(cur, cm, t);
     };
