@@ -13,8 +13,7 @@
 //    with ordinary 16-byte vector loads (kDepth items ahead in registers; on this part they sustain more
 //    bandwidth than direct global->LDS loads) into a ring of kNS LDS stages; four consumer waves compute.
 //    Producers and consumers hand stages over through LDS counters, with no workgroup barrier per tile.
-//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries (a few
-//    items: the boundary itself is latency-bound).  Stage rows are padded by 16 bytes, so the 16-byte operand
+//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries.  Stage rows are padded by 16 bytes, so the 16-byte operand
 //    reads of 8 consecutive lanes fall in distinct banks and use immediate offsets.
 //  * Per tile: C[v, b] = U[b, v] + sum_j W2t[v, j] X[b, j] with v_mfma_f32_32x32x16_bf16 (A = W2 tile from
 //    LDS, stored in permuted row slots; B = the gathered predecessor rows X, resident in registers for the
@@ -62,7 +61,6 @@ struct Ring {
     static constexpr int kDepth = 3;                        // items in flight per producer, in registers
 };
 
-constexpr int kGateItems = 4;  // items of the next position that may be in flight at a position boundary
 constexpr int kConsumers = 4;
 constexpr int kProducers = 4;
 constexpr int kFinalizers = 1;
@@ -379,25 +377,9 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             wait_lgkmcnt0();
             if (lane == 0) lds_add(&ready[i % RG::kNS], 1u);
         };
-        // A position's items past its first kGateItems are not loaded before the consumers have started that
-        // position.  The boundary between positions is a chain of latency-bound memory operations (pick
-        // atomics, barrier polls, the gather of the new rows) that queue behind this CU's outstanding vector
-        // loads, so only a few items may be in flight while it runs.
-        // The gate sits between publish(i) and load(i + D): blocking there must not hold back an item of the
-        // previous position, so at least the first D - 1 items of a position pass.
-        static_assert(kGateItems >= RG::kDepth - 1, "the load gate would block items the consumers wait for");
-        auto gate = [&](int j) {
-            const int kj = j / per_k;
-            if (kj == 0 || j - kj * per_k < kGateItems) return;
-            uint32_t spins = 0;
-            while (lds_load(&released) < (uint32_t)kj) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > spin_limit) {
-                    __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-            }
-        };
+        // The stream runs ahead across position boundaries as far as the ring and the registers allow (kNS + D
+        // items).  Holding back the next position's loads until the boundary had passed helped while the grid
+        // barrier polled counters that every workgroup shared; with the arrival tree it costs 3%.
 #pragma unroll
         for (int d = 0; d < D; ++d)
             if (d < nitems) load(d, regs[d]);
@@ -407,10 +389,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 const int i = i0 + d;
                 if (i < nitems) {
                     publish(i, regs[d]);
-                    if (i + D < nitems) {
-                        gate(i + D);
-                        load(i + D, regs[d]);
-                    }
+                    if (i + D < nitems) load(i + D, regs[d]);
                 }
             }
         }
