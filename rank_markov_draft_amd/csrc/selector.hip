@@ -86,6 +86,23 @@ __device__ __forceinline__ void wave_top_merge(const float* bv, const int* bi, i
     ti = ni;
 }
 
+// The L-th largest of the wave's 64 lane values (bitonic sort across lanes, ascending, then lane 64 - L).
+template <int L>
+__device__ __forceinline__ float wave_lth_largest(float t) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float o = __shfl_xor(t, j);
+            const bool up = (lane & k) == 0 || k == 64;  // ascending block (the last merge ascends)
+            const bool low = (lane & j) == 0;
+            t = (low == up) ? fminf(t, o) : fmaxf(t, o);
+        }
+    }
+    return __shfl(t, 64 - L);
+}
+
 // Top-k (k <= L, L = 16 or 64) of each row, one workgroup per row.  Each wave keeps an exact top-L list (one
 // entry per lane 0..L-1) and its L-th entry as a threshold; every element is compared once against the
 // threshold and the few that beat it are appended to the wave's LDS buffer, which is merged into the list
@@ -138,17 +155,35 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
                 const int q = q0 + j * kTkThreads + (int)threadIdx.x;
                 x[j] = q < nq ? __builtin_nontemporal_load(u4 + q) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             }
+            // Prefilter on values alone: an element can enter the list only if it is >= the threshold value
+            // (ties are then settled by offer's exact order).  After the first few iterations almost no
+            // lane of the wave passes, and one maximum and one ballot cover the lane's 16 elements.
+            float mj[kTkUnroll];
+            float mx = -INFINITY;
 #pragma unroll
             for (int j = 0; j < kTkUnroll; ++j) {
-                const int q = q0 + j * kTkThreads + (int)threadIdx.x;
-                const int id = q < nq ? 4 * q : 0x7FFFFFFC;
-                const bool any = before(x[j].x, id, thv, thi) || before(x[j].y, id + 1, thv, thi) ||
-                                 before(x[j].z, id + 2, thv, thi) || before(x[j].w, id + 3, thv, thi);
-                if (__ballot(any)) {
-                    offer(x[j].x, id);
-                    offer(x[j].y, id + 1);
-                    offer(x[j].z, id + 2);
-                    offer(x[j].w, id + 3);
+                mj[j] = fmaxf(fmaxf(x[j].x, x[j].y), fmaxf(x[j].z, x[j].w));
+                mx = fmaxf(mx, mj[j]);
+            }
+            if (q0 == 0) {
+                // Start the filter at the L-th largest lane maximum of the first chunk: the L lanes at or above
+                // it hold L elements at least that large, so no smaller element can enter the wave's top-L.
+                // Equal values still pass (id bound INT_MAX) and are settled exactly.  Without it every element
+                // of the first chunk is a candidate and the merges of the start dominate the scan.
+                thv = wave_lth_largest<L>(mx);
+                thi = 0x7FFFFFFF;
+            }
+            if (__ballot(mx >= thv)) {
+#pragma unroll
+                for (int j = 0; j < kTkUnroll; ++j) {
+                    if (__ballot(mj[j] >= thv)) {
+                        const int q = q0 + j * kTkThreads + (int)threadIdx.x;
+                        const int id = q < nq ? 4 * q : 0x7FFFFFFC;
+                        offer(x[j].x, id);
+                        offer(x[j].y, id + 1);
+                        offer(x[j].z, id + 2);
+                        offer(x[j].w, id + 3);
+                    }
                 }
             }
         }
