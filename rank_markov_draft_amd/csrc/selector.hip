@@ -364,6 +364,83 @@ __global__ void __launch_bounds__(256) pair_score_kernel(SelectorArgs a) {
     }
 }
 
+// Pair scores on the matrix cores (bf16 weights, r % 16 == 0, 16-byte aligned rows): one workgroup per
+// (row, position, block of 32 predecessors, block of 32 candidates), four waves splitting the rank steps.
+// v_mfma_f32_32x32x16_bf16 with A = the (gated) predecessor rows and B = the candidate rows, both loaded
+// straight from global memory into operand registers (lane l: row l % 32, rank elements 16 s + 8 (l / 32)
+// .. + 7 of step s), no staging.  Gated rows are multiplied by H in fp32 and rounded to bf16, as on the
+// Markov path.  The four partial 32x32 tiles are summed through LDS; accumulator i of lane l is predecessor
+// 8 (i / 4) + 4 (l / 32) + i % 4 and candidate l % 32.
+constexpr int kPairTile = 32;
+__global__ void __launch_bounds__(256) pair_score_mfma_kernel(SelectorArgs a) {
+    __shared__ float part[4][16][64];
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A);
+    const uint16_t* Bm = reinterpret_cast<const uint16_t*>(a.Bemb);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bt = blockIdx.x, b = bt / a.K, t = bt % a.K;
+    const int npred = (t == 0) ? 1 : a.topk;
+    const int i0 = blockIdx.y * kPairTile, j0 = blockIdx.z * kPairTile;
+    if (i0 >= npred) return;
+    const int ni = min(kPairTile, npred - i0), nj = min(kPairTile, a.topk - j0);
+    const int r = a.r;
+    const int32_t* cand_t = a.cand + ((size_t)b * a.K + t) * a.topk;
+    const int rl = lane & 31, half = lane >> 5;
+    const bool pi_ok = rl < ni, cj_ok = rl < nj;
+    const int pid = pi_ok ? ((t == 0) ? a.anchor[b] : a.cand[((size_t)b * a.K + t - 1) * a.topk + i0 + rl]) : 0;
+    const int cid = cj_ok ? cand_t[j0 + rl] : 0;
+    const float* Ht = a.H ? a.H + ((size_t)b * a.K + t) * r : nullptr;
+    const uint16_t* arow = A + (size_t)pid * r + 8 * half;
+    const uint16_t* brow = Bm + (size_t)cid * r + 8 * half;
+    const int nsteps = r / 16;
+    f32x16_t acc = {};
+    constexpr int kBatch = 4;  // operand loads in flight per lane and operand
+    for (int s0 = wave; s0 < nsteps; s0 += 4 * kBatch) {
+        u32x4_t ar[kBatch], br[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int st = s0 + 4 * q;
+            ar[q] = (st < nsteps && pi_ok) ? *reinterpret_cast<const u32x4_t*>(arow + 16 * st) : u32x4_t{0u, 0u, 0u, 0u};
+            br[q] = (st < nsteps && cj_ok) ? *reinterpret_cast<const u32x4_t*>(brow + 16 * st) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int st = s0 + 4 * q;
+            if (st < nsteps) {
+                u32x4_t av = ar[q];
+                if (Ht) {
+                    const float* hp = Ht + 16 * st + 8 * half;
+                    const uint32_t w[4] = {av.x, av.y, av.z, av.w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = bf16_to_f32((uint16_t)(w[e] & 0xFFFFu)) * hp[2 * e];
+                        const float hi = bf16_to_f32((uint16_t)(w[e] >> 16)) * hp[2 * e + 1];
+                        o[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                    }
+                    av = u32x4_t{o[0], o[1], o[2], o[3]};
+                }
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                             __builtin_bit_cast(bf16x8_t, br[q]), acc, 0, 0, 0);
+            }
+        }
+    }
+    // the 16 accumulators of a lane cover predecessors 0 .. 31 of the tile (rows past ni are dropped)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+        const float ub = cj_ok ? a.U[((size_t)b * a.K + t) * a.V + cid] : 0.f;
+        float* out = a.scores + (size_t)b * (a.topk + (size_t)(a.K - 1) * a.topk * a.topk) +
+                     (t == 0 ? 0 : a.topk + (size_t)(t - 1) * a.topk * a.topk);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int pi = 8 * (i / 4) + 4 * half + (i % 4);
+            const float v = part[0][i][lane] + part[1][i][lane] + part[2][i][lane] + part[3][i][lane];
+            if (pi < ni && cj_ok) out[(size_t)(i0 + pi) * a.topk + j0 + rl] = ub + v;
+        }
+    }
+}
+
 // One wave per row: K serial picks.  STAGED: the row's score tables and candidate ids are first copied to
 // LDS with independent loads, so the serial chain runs on LDS latency instead of memory latency.
 template <bool STAGED>
@@ -457,6 +534,11 @@ int topk_supported(int V, int topk) { return topk >= 1 && topk <= V && (topk <= 
 hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
     const dim3 grid(a.B * a.K, (a.topk + kPairBlock - 1) / kPairBlock);
     const bool vec = ((uintptr_t)a.A % 16 == 0) && ((uintptr_t)a.Bemb % 16 == 0) && (a.r % (a.bf16 ? 8 : 4) == 0);
+    if (a.bf16 && vec && a.r % 16 == 0) {
+        const int nt = (a.topk + kPairTile - 1) / kPairTile;
+        hipLaunchKernelGGL(pair_score_mfma_kernel, dim3(a.B * a.K, nt, nt), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.bf16) {
         if (vec) hipLaunchKernelGGL((pair_score_kernel<uint16_t, true>), grid, dim3(256), 0, st, a);
         else hipLaunchKernelGGL((pair_score_kernel<uint16_t, false>), grid, dim3(256), 0, st, a);
