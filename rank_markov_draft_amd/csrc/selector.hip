@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(256) pair_score_mfma_kernel(SelectorArgs a) {
 // LDS with independent loads, so the serial chain runs on LDS latency instead of memory latency.
 template <bool STAGED>
 __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
-    extern __shared__ float wsh[];
+    extern __shared__ __attribute__((aligned(16))) float wsh[];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const size_t tstride = a.topk + (size_t)(a.K - 1) * a.topk * a.topk;
@@ -455,8 +455,26 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
         float* ss = wsh;
         int32_t* cs = reinterpret_cast<int32_t*>(wsh + tstride);
         const int nc = a.K * a.topk;
+        // the copy is one round trip: 16-byte loads, up to 16 per lane in flight
+        constexpr int kBatch = 16;
+        const int n4 = ((uintptr_t)sc % 16 == 0) ? (int)(tstride / 4) : 0;
+        const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(sc);
+        f32x4_t* d4 = reinterpret_cast<f32x4_t*>(ss);
+        for (int i0 = 0; i0 < n4; i0 += 64 * kBatch) {
+            f32x4_t v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int i = i0 + 64 * q + lane;
+                v[q] = i < n4 ? s4[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int i = i0 + 64 * q + lane;
+                if (i < n4) d4[i] = v[q];
+            }
+        }
 #pragma unroll 8
-        for (int i = lane; i < (int)tstride; i += 64) ss[i] = sc[i];
+        for (int i = 4 * n4 + lane; i < (int)tstride; i += 64) ss[i] = sc[i];
 #pragma unroll 4
         for (int i = lane; i < nc; i += 64) cs[i] = cands[i];
         __syncthreads();
