@@ -7,9 +7,10 @@ A step is one draft round of the serving workload: B=128 rows, K=16 positions, v
 r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, sampling at T=1 (block-race draw from softmax) with
 log-probabilities, i.e. dspark_markov_draft: for every position the fused bias-contraction / calibration
 / pick kernel and the cross-workgroup reduction.  Inputs are synthetic (the seeded generator) and are
-resident in HBM before timing starts.  Before every timed round a 1 GiB fill evicts the L2 and the
-256 MB last-level cache, so the round starts with nothing of W2 or U cached; the fill is outside the
-event pair.  The printed line is one JSON object:
+resident in HBM before timing starts.  Before every timed round a 1 GiB read evicts the L2 and the
+256 MB last-level cache, so the round starts with nothing of W2 or U cached; the read is outside the event
+pair.  (A read leaves the caches clean.  A 1 GiB write fill would leave them full of dirty lines whose
+write-back then competes with the timed round's reads; that variant is reported as an extra.)  The printed line is one JSON object:
 
     value          B*K / mean round time (draft tokens per second), from HIP events around each round
     roofline       the fused step kernel against HBM bandwidth: algorithmic bytes of one launch (one
@@ -124,7 +125,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -133,7 +134,10 @@ def main():
         del src, dst
 
     def evict():
-        flush_buf.fill_(1)
+        flush_buf.sum()  # reads 1 GiB
+
+    def evict_dirty():
+        flush_buf.fill_(1.0)  # writes 1 GiB
 
     def to_w(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -209,6 +213,17 @@ def main():
     # back-to-back rounds without eviction (W2 may stay in the last-level cache across rounds)
     ms_b2b, _ = timed_rounds(serving_round, args.steps, flush=False)
 
+    # rounds after a 1 GiB write fill instead of a read (its dirty lines are written back during the round)
+    ms_dirty = []
+    for _ in range(max(3, min(args.steps, 10))):
+        evict_dirty()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        serving_round()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_dirty.append(e0.elapsed_time(e1))
+
     # the same round captured once in a graph and replayed (evicted like the plain enqueue)
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -224,6 +239,7 @@ def main():
         "roofline_tokens_per_s": round(roof_tok_s, 1), "roofline_round_ms": round(roof_round_ms, 4),
         "back_to_back_round_ms": round(float(ms_b2b.mean()), 4),
         "back_to_back_tokens_per_s": round(B * K / (float(ms_b2b.mean()) / 1e3), 1),
+        "after_write_fill_round_ms": round(float(np.mean(ms_dirty)), 4),
         "graph_replay_round_ms": round(float(ms_graph.mean()), 4),
         "graph_replay_tokens_per_s": round(B * K / (float(ms_graph.mean()) / 1e3), 1),
         "timed_wall_s": round(wall, 4),
