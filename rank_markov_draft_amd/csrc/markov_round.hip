@@ -13,8 +13,9 @@
 //    with ordinary 16-byte vector loads (kDepth items ahead in registers; on this part they sustain more
 //    bandwidth than direct global->LDS loads) into a ring of kNS LDS stages; four consumer waves compute.
 //    Producers and consumers hand stages over through LDS counters, with no workgroup barrier per tile.
-//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries.  Stage rows are padded by 16 bytes, so the 16-byte operand
-//    reads of 8 consecutive lanes fall in distinct banks and use immediate offsets.
+//    The stream does not depend on the drafted tokens, so it runs ahead across position boundaries.  Stage
+//    rows are padded by 16 bytes, so the 16-byte operand reads of 8 consecutive lanes fall in distinct banks
+//    and use immediate offsets.
 //  * Per tile: C[v, b] = U[b, v] + sum_j W2t[v, j] X[b, j] with v_mfma_f32_32x32x16_bf16 (A = W2 tile from
 //    LDS, stored in permuted row slots; B = the gathered predecessor rows X, resident in registers for the
 //    position; C seeded with the U tile).  A lane holds one batch row and 16 consecutive vocabulary ids of
