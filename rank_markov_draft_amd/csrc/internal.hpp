@@ -107,10 +107,11 @@ struct RoundArgs {
 };
 // Each (position, row) pick has kWinnerSlots words (workgroup g updates slot g % kWinnerSlots), each on a
 // 128-byte line of its own: every workgroup updates every row once per position, and atomics on one line are
-// serialised where they are performed, so fewer updates per line shorten the end of a position.  A reader
-// takes the largest slot.
+// serialised where they are performed.  A reader takes the largest slot.  More slots shorten the atomics
+// of an idle machine (microbenchmark: 1.8 us with one, 1.1 us with two) but under the stream the extra reads
+// at the start of the next position cost more (serving round: 2 slots +1%, 4 slots +3% over one).
 constexpr int kWinnerStride = 16;
-constexpr int kWinnerSlots = 2;
+constexpr int kWinnerSlots = 1;
 // Grid barrier: workgroup g arrives on group counter g % kBarrierGroups; the last arrival of a group counts
 // on the top counter, and the last arrival there writes every copy of the release word, which each workgroup
 // polls on a line shared with few others.

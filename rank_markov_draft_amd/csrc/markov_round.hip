@@ -25,8 +25,8 @@
 //    form one aligned block whose mass S = sum_v 2^(l_v c - m) (the same exponentials the log-sum-exp needs)
 //    races with one exponential variate, and the winning block's id is drawn by inverse CDF, so one hash
 //    pair and one logarithm serve 16 ids.
-//  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id), spread over two
-//    words per row, gives the global pick with ties to the lower id; log-sum-exp partials go to the
+//  * End of a position: one 64-bit atomicMax per row and workgroup on (ordered key, ~id), each row's word on
+//    its own cache line, gives the global pick with ties to the lower id; log-sum-exp partials go to the
 //    workspace.  A grid barrier then releases the next position, whose workgroups gather W1 rows of the new
 //    tokens.  The barrier is a two-level arrival tree (8 group counters, then a top counter) whose last
 //    arrival writes 8 copies of a release word: every poll reads one line shared by an eighth of the grid, and
