@@ -323,44 +323,73 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         constexpr int NU = RG::kUnitsPerProducer;
         constexpr int D = RG::kDepth;
         u32x4_t regs[D][NU];
-        auto load = [&](int i, u32x4_t (&dst)[NU]) {
-            const int k = i / per_k;
-            const int rem = i - k * per_k;
-            const int rb = rem / ntw;
-            const int t = tile_of(rem - rb * ntw);
-            const int v0 = t * kRTileV;
-            const float* ub = a.U + (size_t)k * a.u_kstride;
+        // Per-lane parts of every unit's global and LDS addresses, computed once: a load then costs one 64-bit
+        // add per unit (index arithmetic per item, with its 64-bit multiplies, took issue cycles from the
+        // consumer wave on the same SIMD).
+        // W2 unit u covers tile rows 64u / (2 RK) + lane / (2 RK), 8 bf16 at column 8 (lane mod 2 RK) (2 RK
+        // divides 64); U unit RK + q covers rows 8q + lane / 8, 4 floats at column 4 (lane mod 8).
+        static_assert(64 % (2 * RK) == 0, "a W2 unit holds whole rows");
+        const int urow = lane >> 3, ucol = 4 * (lane & 7);
+        const uint32_t w2lane = 2u * (uint32_t)((lane / (2 * RK)) * r + 8 * (lane % (2 * RK)));
+        const uint64_t ulane = 4ull * ((uint64_t)urow * (uint64_t)a.u_stride + (uint64_t)ucol);
+        uint32_t soff[NU];   // byte offset in a stage
 #pragma unroll
-            for (int n = 0; n < NU; ++n) {
-                const int u = p + 4 * n;
-                if (u < RK) {
-                    const int P = u * 64 + lane;
-                    const int rho = P / (2 * RK), c = P % (2 * RK);
-                    const int vrow = min(v0 + rho, a.V - 1);
+        for (int n = 0; n < NU; ++n) {
+            const int u = p + 4 * n;
+            if (u < RK) {
+                const int P = u * 64 + lane;
+                const int rho = P / (2 * RK), c = P % (2 * RK);
+                soff[n] = (uint32_t)(w2_slot(rho) * RG::kW2Row + 16 * c);
+            } else {
+                soff[n] = (uint32_t)(RG::kW2Bytes + (8 * (u - RK) + urow) * RG::kURow + 16 * (lane & 7));
+            }
+        }
+        // the next item to load: position, row block, tile slot
+        int lk = 0, lrb = 0, lj = 0;
+        auto load_next = [&](u32x4_t (&dst)[NU]) {
+            const int v0 = tile_of(lj) * kRTileV;
+            const int b0 = lrb * kRRows;
+            if (v0 + kRTileV <= a.V && b0 + kRRows <= a.B) {
+                const uint8_t* w2b = reinterpret_cast<const uint8_t*>(a.W2t + (size_t)v0 * r);
+                const uint8_t* ub = reinterpret_cast<const uint8_t*>(a.U + (size_t)lk * a.u_kstride + (size_t)b0 * a.u_stride + v0);
+#pragma unroll
+                for (int n = 0; n < NU; ++n) {
+                    const int u = p + 4 * n;
                     // W2 is re-read every position: a cacheable load lets it stay in the last-level cache
-                    dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * c);
-                } else if (u < RG::kUnits) {
-                    const int q = u - RK;
-                    const int b = min(rb * kRRows + q * 8 + (lane >> 3), a.B - 1);
-                    const int col = min(v0 + 4 * (lane & 7), a.V - 4);
-                    dst[n] = load_nt_u32x4(ub + (size_t)b * a.u_stride + col);
+                    if (u < RK)
+                        dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
+                    else if (u < RG::kUnits)
+                        dst[n] = load_nt_u32x4(ub + (size_t)(u - RK) * 32 * (size_t)a.u_stride + ulane);
+                }
+            } else {
+                // a tile past the vocabulary's end or a row block past the batch: clamped rows and columns
+#pragma unroll
+                for (int n = 0; n < NU; ++n) {
+                    const int u = p + 4 * n;
+                    if (u < RK) {
+                        const int P = u * 64 + lane;
+                        const int vrow = min(v0 + P / (2 * RK), a.V - 1);
+                        dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * (P % (2 * RK)));
+                    } else if (u < RG::kUnits) {
+                        const int b = min(b0 + (u - RK) * 8 + urow, a.B - 1);
+                        const int col = min(v0 + ucol, a.V - 4);
+                        dst[n] = load_nt_u32x4(a.U + (size_t)lk * a.u_kstride + (size_t)b * a.u_stride + col);
+                    }
+                }
+            }
+            if (++lj == ntw) {
+                lj = 0;
+                if (++lrb == nrb) {
+                    lrb = 0;
+                    ++lk;
                 }
             }
         };
         auto store = [&](int i, const u32x4_t (&src)[NU]) {
             uint8_t* st = ring + (i % RG::kNS) * RG::kStage;
 #pragma unroll
-            for (int n = 0; n < NU; ++n) {
-                const int u = p + 4 * n;
-                if (u < RK) {
-                    const int P = u * 64 + lane;
-                    const int rho = P / (2 * RK), c = P % (2 * RK);
-                    *reinterpret_cast<u32x4_t*>(st + w2_slot(rho) * RG::kW2Row + 16 * c) = src[n];
-                } else if (u < RG::kUnits) {
-                    const int q = u - RK;
-                    *reinterpret_cast<u32x4_t*>(st + RG::kW2Bytes + (8 * q + (lane >> 3)) * RG::kURow + 16 * (lane & 7)) = src[n];
-                }
-            }
+            for (int n = 0; n < NU; ++n)
+                if (p + 4 * n < RG::kUnits) *reinterpret_cast<u32x4_t*>(st + soff[n]) = src[n];
         };
         auto publish = [&](int i, const u32x4_t (&src)[NU]) {
             if (i >= RG::kNS) {
@@ -383,14 +412,14 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         // barrier polled counters that every workgroup shared; with the arrival tree it costs 3%.
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (d < nitems) load(d, regs[d]);
+            if (d < nitems) load_next(regs[d]);
         for (int i0 = 0; i0 < nitems; i0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int i = i0 + d;
                 if (i < nitems) {
                     publish(i, regs[d]);
-                    if (i + D < nitems) load(i + D, regs[d]);
+                    if (i + D < nitems) load_next(regs[d]);
                 }
             }
         }
