@@ -175,6 +175,16 @@ int dspark_markov_logits(const float* U_k, int64_t u_stride, const void* W1, con
  */
 int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, void* stream);
 
+/*
+ * Measurement utility, not a step of the method: reads the device buffer a (a_bytes) with ordinary 16-byte
+ * loads and then b (b_bytes) with non-temporal ones, once, and writes nothing but possibly one word of sink
+ * (a device uint32).  Timing it over the operands of a draft round (W2 and the base logits of each position)
+ * gives the rate at which this part streams those bytes, the practical ceiling beside the nominal HBM peak.
+ * Sizes must be multiples of 16 and the buffers 16-byte aligned (DSPARK_EINVAL otherwise); a NULL buffer is
+ * allowed only with size 0.
+ */
+int dspark_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------------------------------ */
 /* gate                                                                                             */
 /* ------------------------------------------------------------------------------------------------ */

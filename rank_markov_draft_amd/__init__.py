@@ -50,6 +50,7 @@ def _load_lib():
                                 vp], i32),
         "dspark_markov_logits": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, sz, vp], i32),
         "dspark_pack_w2": ([vp, i32, i32, i32, vp, vp], i32),
+        "dspark_stream_read": ([vp, sz, vp, sz, vp, vp], i32),
         "dspark_gate": ([vp, vp, i32, i32, i32, vp, vp], i32),
         "dspark_topk_workspace_bytes": ([i32, i32, i32], sz),
         "dspark_topk": ([vp, i64, i32, i32, i32, vp, vp, vp, sz, vp], i32),
@@ -255,6 +256,15 @@ def dspark_pack_w2(W2_rv, *, out=None, stream=None):
         out = torch.empty((V, r), dtype=W2_rv.dtype, device=W2_rv.device)
     _check(_lib.dspark_pack_w2(_p(W2_rv), V, r, _wdtype(W2_rv), _p(out), _stream(stream)), "dspark_pack_w2")
     return out
+
+
+def dspark_stream_read(a, b, sink, *, stream=None):
+    """Reads the contiguous device tensors a and b once (measurement utility); sink: a 1-element int32 tensor."""
+    for t, n in ((a, "a"), (b, "b"), (sink, "sink")):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    _check(_lib.dspark_stream_read(_p(a), a.numel() * a.element_size(), _p(b), b.numel() * b.element_size(), _p(sink),
+                                   _stream(stream)), "dspark_stream_read")
 
 
 def dspark_gate(h, Wg, *, out=None, stream=None):

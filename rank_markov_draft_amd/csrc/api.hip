@@ -357,6 +357,16 @@ int dspark_pack_w2(const void* src_rv, int V, int r, int wdtype, void* dst_vr, v
     return DSPARK_OK;
 }
 
+int dspark_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, void* stream) {
+    g_err[0] = 0;
+    if (!sink || (a_bytes && !a) || (b_bytes && !b)) return fail(DSPARK_EINVAL, "NULL buffer");
+    if (a_bytes % 16 || b_bytes % 16) return fail(DSPARK_EINVAL, "sizes must be multiples of 16 bytes");
+    if (!aligned16(a) || !aligned16(b)) return fail(DSPARK_EINVAL, "buffers must be 16-byte aligned");
+    hipError_t e = launch_stream_read(a, a_bytes, b, b_bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "stream read launch");
+    return DSPARK_OK;
+}
+
 int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
                         const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode, uint64_t seed,
                         float temperature, int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes,

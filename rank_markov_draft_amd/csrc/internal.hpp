@@ -129,6 +129,7 @@ hipError_t launch_markov_step_valu(const StepArgsValu& a, bool bf16, int mode, b
 hipError_t launch_markov_reduce(const ReduceArgs& a, int B, hipStream_t st);
 
 hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes, void* dst, hipStream_t st);
+hipError_t launch_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, hipStream_t st);
 
 // gate: H = sigmoid(h Wg)
 hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, hipStream_t st);

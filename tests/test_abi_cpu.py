@@ -132,3 +132,11 @@ def test_selector_gate_topk_argument_errors(lib):
     p = lib.dspark_pack_w2
     assert p(None, 10, 10, 1, FAKE, None) == 1
     assert p(FAKE, 10, 10, 9, FAKE, None) == 1
+
+
+def test_stream_read_argument_errors(lib):
+    f = lib.dspark_stream_read
+    assert f(FAKE, 64, FAKE, 64, None, None) == 1                                  # no sink
+    assert f(None, 64, FAKE, 64, FAKE, None) == 1                                  # NULL with a size
+    assert f(FAKE, 60, FAKE, 64, FAKE, None) == 1 and "16" in _err(lib)           # not a multiple of 16
+    assert f(ctypes.c_void_p(0x1008), 64, FAKE, 64, FAKE, None) == 1              # misaligned
