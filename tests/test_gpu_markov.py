@@ -224,3 +224,21 @@ def test_sampling_temperature_extremes(D, T):
     tok, lp = host(tok), host(lp)
     ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=99, temperature=T, follow=tok)
     check_draft(tok, lp, ref, what=f"T={T}")
+
+
+@pytest.mark.parametrize("shape", [(128, 3, 4096, 256), (5, 3, 1001, 64)], ids=["round", "per-position"])
+def test_timed_draft_matches_plain_draft(D, shape):
+    """The bench's timed entry point drafts exactly what dspark_markov_draft drafts and reports its launches."""
+    import torch
+
+    B, K, V, r = shape
+    w = S.strong("serving", B=B, K=K, V=V, r=r)
+    args = (t_f32(w.U), t_w(w.W1), t_w(np.ascontiguousarray(w.W2.T)), t_i32(w.anchor))
+    kw = dict(w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_SAMPLE, seed=w.noise_seed)
+    tok, lp = D.dspark_markov_draft(*args, **kw)
+    tok2, lp2, kms, nl, rms = D.dspark_markov_draft_timed(*args, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tok), host(tok2)) and np.array_equal(host(lp), host(lp2))
+    round_path = V % 4 == 0 and r % 16 == 0 and r <= 256
+    assert nl == (1 if round_path else K)
+    assert 0.0 < kms <= rms * 1.05
