@@ -4,21 +4,25 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
 
 A step is one draft round of the serving workload: B=128 rows, K=16 positions, vocabulary V=151936, rank
-r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, sampling at T=1 (block-race draw from softmax) with
-log-probabilities, i.e. dspark_markov_draft: for every position the fused bias-contraction / calibration
-/ pick kernel and the cross-workgroup reduction.  Inputs are synthetic (the seeded generator) and are
-resident in HBM before timing starts.  Before every timed round a 1 GiB read evicts the L2 and the
-256 MB last-level cache, so the round starts with nothing of W2 or U cached; the read is outside the event
-pair.  (A read leaves the caches clean.  A 1 GiB write fill would leave them full of dirty lines whose
-write-back then competes with the timed round's reads; that variant is reported as an extra.)  The printed line is one JSON object:
+r=256, bf16 W1/W2 (W2 held transposed, [V, r]), fp32 base logits, sampling at T=1 (block-race draw from
+softmax) with log-probabilities, i.e. one dspark_markov_draft call: a single persistent launch that, for
+every position, gathers the predecessor rows, runs the fused bias contraction / calibration / pick and the
+cross-workgroup reduction.  Inputs are synthetic (the seeded generator) and are resident in HBM before timing
+starts.  Before every timed round a 1 GiB read evicts the L2 and the 256 MB last-level cache, so the round
+starts with nothing of W2 or U cached; the read is outside the event pair.  (A read leaves the caches clean.
+A 1 GiB write fill would leave them full of dirty lines whose write-back then competes with the timed round's
+reads; that variant is reported as an extra.)  The printed line is one JSON object:
 
     value          B*K / mean round time (draft tokens per second), from HIP events around each round
-    roofline       the fused step kernel against HBM bandwidth: algorithmic bytes of one launch (one
-                   position: W2 + U_k + gathered W1 rows + predecessors + outputs) over the kernel's mean
-                   duration, timed with HIP events on the library's stream around each launch
+    roofline       the round kernel against HBM bandwidth: algorithmic bytes of one launch (16 positions of
+                   W2 + U_k + gathered W1 rows + predecessors + outputs) over the kernel's mean duration,
+                   timed with HIP events on the library's stream around each launch; traffic = the
+                   counter-measured bytes per launch recorded for the current kernel source
     cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload, on this host's cores
-    extras         the other measured shapes (batch-1, top-16 Selector, gated head) and the back-to-back
-                   (no eviction) rate
+    extras         the back-to-back (no eviction), write-fill and graph-replay rates, the practical streaming
+                   ceiling of the round's bytes (read_ceiling), and the other measured shapes (greedy,
+                   confidence head, prefix scheduler, top-16 Selector and its top-k sweep, gated head,
+                   batch 1)
 """
 import argparse
 import hashlib
