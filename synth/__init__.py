@@ -168,7 +168,7 @@ WORKLOADS = {
     # B=1, K=16, V=151936, r=256, bf16 weights, greedy (GEMV-shaped step)
     "batch1": dict(B=1, K=16, V=151936, r=256, wdtype=BF16, sigma_w=0.02, n_hot=16, mode=GREEDY,
                    seed=0xD5A10002),
-    # B=128, K=16, V=151936, r=256, Gumbel-max at T=1 (the serving batch)
+    # B=128, K=16, V=151936, r=256, sampling at T=1 (the serving batch)
     "serving": dict(B=128, K=16, V=151936, r=256, wdtype=BF16, sigma_w=0.02, n_hot=16, mode=SAMPLE,
                     seed=0xD5A10003),
     # top-16 Selector, ungated, greedy walk (A := W1, Bemb := W2^T of this seed)

@@ -169,8 +169,13 @@ def _full_draft_check(D, w, rows, mode, seed, H=None, Hd=None):
 
 
 def test_full_serving_sampled_rows(D, serving):
-    """B=128, K=16, V=151936, r=256, Gumbel-max T=1: every position of three sampled rows."""
+    """B=128, K=16, V=151936, r=256, sampling at T=1 (the block-race draw): every position of three rows."""
     _full_draft_check(D, serving, [0, 77, 127], S.SAMPLE, serving.noise_seed)
+
+
+def test_full_serving_greedy_sampled_rows(D, serving):
+    """The serving shape with greedy picks (the bench's greedy line): every position of two rows."""
+    _full_draft_check(D, serving, [5, 100], S.GREEDY, 0)
 
 
 def test_full_serving_logits_sampled_rows(D, serving):
