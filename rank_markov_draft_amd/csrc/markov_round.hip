@@ -652,25 +652,46 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 }
             }
             const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(a.W1 + (size_t)pv * r);
-#pragma unroll
-            for (int kk = 0; kk < RK; ++kk) {
-                u32x4_t raw = valid_b ? wrow[2 * kk + half] : u32x4_t{0u, 0u, 0u, 0u};
-                if (GATED && valid_b) {
-                    const float* hrow = a.H + ((size_t)b * a.K + k) * r + 16 * kk + 8 * half;
-                    const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(hrow);
-                    const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(hrow + 4);
-                    const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            if constexpr (GATED) {
+                // X = bf16(W1[a] * H) in phases of kPh 16-value chunks.  Each phase issues all of its loads (W1
+                // row chunks, H chunks) before its multiplies, so the gather costs the pick read and one memory
+                // round trip per phase, rather than one per chunk; four phases fit the register budget at
+                // r = 256.  Rows past the batch load row 0 and are zeroed.
+                constexpr int kPh = RK >= 4 ? RK / 4 : 1;
+                const float* hrow = a.H + ((size_t)(valid_b ? b : 0) * a.K + k) * r + 8 * half;
+                auto apply = [&](const u32x4_t raw, const f32x4_t h0, const f32x4_t h1) -> bf16x8_t {
+                    const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
                     const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
                     uint32_t o32[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float lo = bf16_to_f32((uint16_t)(w32[e] & 0xFFFFu)) * hv[2 * e];
-                        const float hi = bf16_to_f32((uint16_t)(w32[e] >> 16)) * hv[2 * e + 1];
+                        const float lo = bf16_to_f32((uint16_t)(w32[e] & 0xFFFFu)) * hf[2 * e];
+                        const float hi = bf16_to_f32((uint16_t)(w32[e] >> 16)) * hf[2 * e + 1];
                         o32[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
                     }
-                    raw = u32x4_t{o32[0], o32[1], o32[2], o32[3]};
+                    const u32x4_t o = valid_b ? u32x4_t{o32[0], o32[1], o32[2], o32[3]} : u32x4_t{0u, 0u, 0u, 0u};
+                    return __builtin_bit_cast(bf16x8_t, o);
+                };
+#pragma unroll
+                for (int p0 = 0; p0 < RK; p0 += kPh) {
+                    u32x4_t raw[kPh];
+#pragma unroll
+                    for (int q = 0; q < kPh; ++q) raw[q] = wrow[2 * (p0 + q) + half];
+                    f32x4_t hv[2 * kPh];
+#pragma unroll
+                    for (int q = 0; q < kPh; ++q) {
+                        hv[2 * q] = *reinterpret_cast<const f32x4_t*>(hrow + 16 * (p0 + q));
+                        hv[2 * q + 1] = *reinterpret_cast<const f32x4_t*>(hrow + 16 * (p0 + q) + 4);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kPh; ++q) xf[p0 + q] = apply(raw[q], hv[2 * q], hv[2 * q + 1]);
                 }
-                xf[kk] = __builtin_bit_cast(bf16x8_t, raw);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < RK; ++kk) {
+                    const u32x4_t raw = valid_b ? wrow[2 * kk + half] : u32x4_t{0u, 0u, 0u, 0u};
+                    xf[kk] = __builtin_bit_cast(bf16x8_t, raw);
+                }
             }
             if (SAMPLE) k2 = noise_key2(a.k0, (uint32_t)b, (uint32_t)k);
         }
