@@ -258,7 +258,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
                           aligned16(U) && V % 4 == 0 && (!H || aligned16(H)) && coop_supported();
     if (round_ok) {
         const int ntiles = (V + 31) / 32;
-        int G = round_max_coresident(r, sample, H != nullptr);
+        int G = round_max_coresident(r, sample, H != nullptr, round_small_block(B));
         if (G > round_gmax()) G = round_gmax();
         if (G > ntiles) G = ntiles;
         if (G >= 1) {

@@ -118,8 +118,9 @@ constexpr int kWinnerSlots = 1;
 constexpr int kBarrierGroups = 8;
 constexpr int kCounterStride = 32;  // words between counters (128 bytes)
 int round_supported_r(int r);
-int round_lds_bytes(int r);
-int round_max_coresident(int r, bool sample, bool gated);
+// A batch of at most 8 rows takes the round kernel's small-block form (one U unit per item, deeper stream).
+inline bool round_small_block(int B) { return B <= 8; }
+int round_max_coresident(int r, bool sample, bool gated, bool small);
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
                                hipEvent_t ev_end);
 

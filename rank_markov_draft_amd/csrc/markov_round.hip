@@ -48,18 +48,22 @@ constexpr int kRTileV = 32;
 constexpr int kRRows = 128;
 constexpr float kNegBig = -1e30f;  // start of a running max; stays finite when scaled by log2(e)/T
 
-template <int RK>
+// UR = U units (8 rows each) per item: 16 for a full 128-row block; 1 for a batch of at most 8 rows, whose
+// items are W2 almost only: then the registers and LDS that U rows would take hold more items instead (six in
+// flight per producer, eight stages), since a stream of small items is bound by the bytes in flight.
+template <int RK, int UR = 16>
 struct Ring {
-    static constexpr int kNS = 4;
+    static_assert(UR == 16 || UR == 1, "full or small row block");
+    static constexpr int kNS = UR == 16 ? 4 : 8;
     static constexpr int kW2Row = 32 * RK + 16;            // one W2 row (r = 16 RK bf16) + 16-byte pad
     static constexpr int kW2Bytes = kRTileV * kW2Row;      // 32 rows
     static constexpr int kURow = 4 * kRTileV + 16;          // one U row of the tile (32 floats) + 16-byte pad
-    static constexpr int kUBytes = kRRows * kURow;          // 128 rows
+    static constexpr int kUBytes = 8 * UR * kURow;          // 8 UR rows
     static constexpr int kStage = kW2Bytes + kUBytes;
-    // one item = RK W2 units (64 lanes x 16 B) + 16 U units (8 rows x 128 B); producer p takes units p, p + 4, ...
-    static constexpr int kUnits = RK + 16;
+    // one item = RK W2 units (64 lanes x 16 B) + UR U units (8 rows x 128 B); producer p takes units p, p + 4, ...
+    static constexpr int kUnits = RK + UR;
     static constexpr int kUnitsPerProducer = (kUnits + 3) / 4;
-    static constexpr int kDepth = 3;                        // items in flight per producer, in registers
+    static constexpr int kDepth = UR == 16 ? 3 : 6;         // items in flight per producer, in registers
 };
 
 constexpr int kConsumers = 4;
@@ -217,15 +221,27 @@ __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) 
     }
 }
 
-template <int RK, int MODE, bool GATED>
+template <int RK, int MODE, bool GATED, int UR>
 __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArgs a) {
-    using RG = Ring<RK>;
+    using RG = Ring<RK, UR>;
     constexpr bool SAMPLE = MODE == kModeSample;
+    // Consumer sets: a small block (at most 8 rows) leaves three of the four consumer waves without rows, so
+    // with greedy picks each wave instead forms a set of its own on the same 32 rows and takes every fourth tile
+    // of a position (slots s, s + 4, ...), handing its per-row results to set 0 through LDS at the end of the
+    // position.  Sampling and the gate keep one set: the sampling epilogue and the gated gather hold more
+    // registers, and with the hand-over code the kernel would spill at three waves per SIMD.
+    constexpr int SETS = (UR == 1 && !SAMPLE && !GATED) ? 4 : 1;
+    constexpr int kRowWaves = kConsumers / SETS;  // consumer waves of one set (32 rows each)
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kNS * RG::kStage];
     __shared__ uint32_t ready[RG::kNS];  // +1 per producer per filled stage
     __shared__ uint32_t freed[RG::kNS];  // +1 per consumer wave per consumed stage
     __shared__ uint32_t stepdone;        // +1 per consumer wave per finished position
     __shared__ uint32_t released;        // last position whose predecessors are known (set by consumer wave 0)
+    // sets 1 .. SETS-1 hand their per-row results of a position to set 0 here (double-buffered by segment
+    // parity): key, id (bits), logit of the pick, base-2 max and sum of the log-sum-exp
+    constexpr int kHand = SETS > 1 ? SETS - 1 : 1;
+    __shared__ float mx[SETS > 1 ? 2 : 1][kHand][SETS > 1 ? kRowWaves : 1][5][32];
+    __shared__ uint32_t mput[kHand][kRowWaves], mgot[kHand][kRowWaves];  // segments written / read
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -246,6 +262,10 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     if (threadIdx.x < RG::kNS) {
         ready[threadIdx.x] = 0u;
         freed[threadIdx.x] = 0u;
+    }
+    if (threadIdx.x < kHand * kRowWaves) {
+        (&mput[0][0])[threadIdx.x] = 0u;
+        (&mgot[0][0])[threadIdx.x] = 0u;
     }
     if (threadIdx.x == 0) {
         stepdone = 0u;
@@ -349,27 +369,51 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         auto load_next = [&](u32x4_t (&dst)[NU]) {
             const int v0 = tile_of(lj) * kRTileV;
             const int b0 = lrb * kRRows;
-            if (v0 + kRTileV <= a.V && b0 + kRRows <= a.B) {
-                const uint8_t* w2b = reinterpret_cast<const uint8_t*>(a.W2t + (size_t)v0 * r);
-                const uint8_t* ub = reinterpret_cast<const uint8_t*>(a.U + (size_t)lk * a.u_kstride + (size_t)b0 * a.u_stride + v0);
+            if constexpr (UR == 16) {
+                if (v0 + kRTileV <= a.V && b0 + kRRows <= a.B) {
+                    const uint8_t* w2b = reinterpret_cast<const uint8_t*>(a.W2t + (size_t)v0 * r);
+                    const uint8_t* ub = reinterpret_cast<const uint8_t*>(a.U + (size_t)lk * a.u_kstride + (size_t)b0 * a.u_stride + v0);
 #pragma unroll
-                for (int n = 0; n < NU; ++n) {
-                    const int u = p + 4 * n;
-                    // W2 is re-read every position: a cacheable load lets it stay in the last-level cache
-                    if (u < RK)
-                        dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
-                    else if (u < RG::kUnits)
-                        dst[n] = load_nt_u32x4(ub + (size_t)(u - RK) * 32 * (size_t)a.u_stride + ulane);
+                    for (int n = 0; n < NU; ++n) {
+                        const int u = p + 4 * n;
+                        // W2 is re-read every position: a cacheable load lets it stay in the last-level cache
+                        if (u < RK)
+                            dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
+                        else if (u < RG::kUnits)
+                            dst[n] = load_nt_u32x4(ub + (size_t)(u - RK) * 32 * (size_t)a.u_stride + ulane);
+                    }
+                } else {
+                    // a tile past the vocabulary's end or a row block past the batch: clamped rows and columns
+#pragma unroll
+                    for (int n = 0; n < NU; ++n) {
+                        const int u = p + 4 * n;
+                        if (u < RK) {
+                            const int P = u * 64 + lane;
+                            const int vrow = min(v0 + P / (2 * RK), a.V - 1);
+                            dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * (P % (2 * RK)));
+                        } else if (u < RG::kUnits) {
+                            const int b = min(b0 + (u - RK) * 8 + urow, a.B - 1);
+                            const int col = min(v0 + ucol, a.V - 4);
+                            dst[n] = load_nt_u32x4(a.U + (size_t)lk * a.u_kstride + (size_t)b * a.u_stride + col);
+                        }
+                    }
                 }
             } else {
-                // a tile past the vocabulary's end or a row block past the batch: clamped rows and columns
+                // small block: W2 units take the precomputed addresses whenever the tile is whole; the U unit
+                // (rows 0..7 of the block) clamps its rows to the batch
+                const uint8_t* w2b = reinterpret_cast<const uint8_t*>(a.W2t + (size_t)v0 * r);
+                const bool vfull = v0 + kRTileV <= a.V;
 #pragma unroll
                 for (int n = 0; n < NU; ++n) {
                     const int u = p + 4 * n;
                     if (u < RK) {
-                        const int P = u * 64 + lane;
-                        const int vrow = min(v0 + P / (2 * RK), a.V - 1);
-                        dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * (P % (2 * RK)));
+                        if (vfull) {
+                            dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
+                        } else {
+                            const int P = u * 64 + lane;
+                            const int vrow = min(v0 + P / (2 * RK), a.V - 1);
+                            dst[n] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vrow * r + 8 * (P % (2 * RK)));
+                        }
                     } else if (u < RG::kUnits) {
                         const int b = min(b0 + (u - RK) * 8 + urow, a.B - 1);
                         const int col = min(v0 + ucol, a.V - 4);
@@ -393,7 +437,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         };
         auto publish = [&](int i, const u32x4_t (&src)[NU]) {
             if (i >= RG::kNS) {
-                const uint32_t need = (uint32_t)kConsumers * (uint32_t)(i / RG::kNS);
+                const uint32_t need = (uint32_t)kRowWaves * (uint32_t)(i / RG::kNS);  // one set consumes an item
                 uint32_t spins = 0;
                 while (lds_load(&freed[i % RG::kNS]) < need) {
                     __builtin_amdgcn_s_sleep(1);
@@ -437,9 +481,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     int bslot = 0, btile = -1;   // best id = 32 btile + 16 half + bslot
     const float c = a.c;
     const int rho = lane & 31;
-    const int rr = wave * 32 + rho;                                      // this lane's row of the 128-row block
+    const int cset = SETS > 1 ? wave / kRowWaves : 0;                    // tile slots cset, cset + SETS, ...
+    const int wrow = SETS > 1 ? wave % kRowWaves : wave;
+    const int rr = wrow * 32 + rho;                                      // this lane's row of the 128-row block
     const int a_off = rho * RG::kW2Row + 16 * half;                      // its A-operand row in a stage
-    const int u_off = RG::kW2Bytes + rr * RG::kURow + 64 * half;        // its 16 U values in a stage
+    // its 16 U values in a stage (a small block holds rows 0..7 only; the rows after them are past the batch)
+    const int u_off = RG::kW2Bytes + (UR == 16 ? rr : min(rr, 8 * UR - 1)) * RG::kURow + 64 * half;
 
     auto wait_ready = [&](int i) {
         const uint32_t need = (uint32_t)kProducers * (uint32_t)(i / RG::kNS + 1);
@@ -542,18 +589,18 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         btile = better ? t : btile;
     };
 
-    // Tile tt's epilogue in one straight-line block with the operand reads and the MFMAs of tile tt + 1 (into
-    // nxt), so the matrix cores' dependent accumulation chain runs under the vector ALUs' work.
-    auto pipelined = [&](f32x16_t& cur, f32x16_t& nxt, int i, int t) {
+    // A tile's epilogue in one straight-line block with the operand reads and the MFMAs of the set's next tile
+    // (item in, into nxt), so the matrix cores' dependent accumulation chain runs under the vector ALUs' work.
+    auto pipelined = [&](f32x16_t& cur, f32x16_t& nxt, int in, int t) {
         const std::integral_constant<bool, false> kUnmasked{};
         // The next tile's reads first (its U tile and the first two A operands), then the head of this tile's
         // epilogue while they land.  Then 16 steps, each: the A operand two MFMAs ahead, one MFMA and a share
         // of the epilogue's vector work.  The scheduling barriers keep that order: left alone, the scheduler
         // reads each A operand right before its MFMA and stalls the wave on every read.
-        nxt = read_u(i + 1);
+        nxt = read_u(in);
         bf16x8_t fr[RK];
-        fr[0] = frag(i + 1, 0);
-        if (RK > 1) fr[1] = frag(i + 1, 1);
+        fr[0] = frag(in, 0);
+        if (RK > 1) fr[1] = frag(in, 1);
         __builtin_amdgcn_sched_barrier(0);
         float mc;
         const float cm = tile_head(cur, t, kUnmasked, mc);
@@ -561,7 +608,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         int sel = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (j + 2 < RK) fr[j + 2] = frag(i + 1, j + 2);
+            if (j + 2 < RK) fr[j + 2] = frag(in, j + 2);
             if (j < RK) nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], xf[j], nxt, 0, 0, 0);
             if (SAMPLE) {
                 // steps 0-7: masses of slots 2j, 2j+1; step 8: the block's variates; steps 8-15: inverse CDF
@@ -613,7 +660,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         const int i0 = seg * ntw;
         const int b = rb * kRRows + rr;
         const bool valid_b = b < a.B;
-        const bool wave_live = rb * kRRows + wave * 32 < a.B;
+        const bool wave_live = rb * kRRows + wrow * 32 < a.B;
 
         // a new position (or row block): wait for the previous position's picks, then gather X.  Consumer wave 0
         // polls this workgroup's copy of the release word; the other consumer waves wait for its LDS flag.
@@ -704,45 +751,88 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         bslot = 0;
         btile = -1;
 
-        // Software pipeline over the segment's tiles, unrolled by two so the accumulator sets alternate.
+        // Software pipeline over the segment's tiles (with several sets: over the set's tile slots cset,
+        // cset + SETS, ...), unrolled by two so the accumulator sets alternate.
         f32x16_t acc_a, acc_b;
         const std::integral_constant<bool, true> kMasked{};
         const std::integral_constant<bool, false> kUnmasked{};
-        wait_ready(i0);
-        if (wave_live) {
-            acc_a = read_u(i0);
+        if constexpr (SETS == 1) {
+            wait_ready(i0);
+            if (wave_live) {
+                acc_a = read_u(i0);
 #pragma unroll
-            for (int j = 0; j < RK; ++j) acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i0, j), xf[j], acc_a, 0, 0, 0);
-        }
-        release(i0);
-        int tt = 0;
-        for (; tt + 2 < ntw; tt += 2) {
-            wait_ready(i0 + tt + 1);
-            if (wave_live) pipelined(acc_a, acc_b, i0 + tt, tile_of(tt));
-            release(i0 + tt + 1);
-            wait_ready(i0 + tt + 2);
-            if (wave_live) pipelined(acc_b, acc_a, i0 + tt + 1, tile_of(tt + 1));
-            release(i0 + tt + 2);
-        }
-        // one or two tiles left, the first in acc_a; only the segment's last tile can be the vocabulary's tail
-        const bool tail = tile_of(ntw - 1) == a.ntiles - 1 && a.ntiles * kRTileV > a.V;
-        if (tt + 1 < ntw) {
-            wait_ready(i0 + tt + 1);
-            if (wave_live) pipelined(acc_a, acc_b, i0 + tt, tile_of(tt));
-            release(i0 + tt + 1);
-            if (wave_live) {
-                if (tail) last(acc_b, tile_of(tt + 1), kMasked);
-                else last(acc_b, tile_of(tt + 1), kUnmasked);
+                for (int j = 0; j < RK; ++j) acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i0, j), xf[j], acc_a, 0, 0, 0);
             }
-        } else if (tt < ntw) {
-            if (wave_live) {
-                if (tail) last(acc_a, tile_of(tt), kMasked);
-                else last(acc_a, tile_of(tt), kUnmasked);
+            release(i0);
+            int tt = 0;
+            for (; tt + 2 < ntw; tt += 2) {
+                wait_ready(i0 + tt + 1);
+                if (wave_live) pipelined(acc_a, acc_b, i0 + tt + 1, tile_of(tt));
+                release(i0 + tt + 1);
+                wait_ready(i0 + tt + 2);
+                if (wave_live) pipelined(acc_b, acc_a, i0 + tt + 2, tile_of(tt + 1));
+                release(i0 + tt + 2);
+            }
+            // one or two tiles left, the first in acc_a; only the segment's last tile can be the vocabulary's tail
+            const bool tail = tile_of(ntw - 1) == a.ntiles - 1 && a.ntiles * kRTileV > a.V;
+            if (tt + 1 < ntw) {
+                wait_ready(i0 + tt + 1);
+                if (wave_live) pipelined(acc_a, acc_b, i0 + tt + 1, tile_of(tt));
+                release(i0 + tt + 1);
+                if (wave_live) {
+                    if (tail) last(acc_b, tile_of(tt + 1), kMasked);
+                    else last(acc_b, tile_of(tt + 1), kUnmasked);
+                }
+            } else if (tt < ntw) {
+                if (wave_live) {
+                    if (tail) last(acc_a, tile_of(tt), kMasked);
+                    else last(acc_a, tile_of(tt), kUnmasked);
+                }
+            }
+        } else {
+            const int nts = (ntw - cset + SETS - 1) / SETS;
+            auto slot = [&](int u) { return cset + SETS * u; };
+            if (nts > 0) {
+                wait_ready(i0 + slot(0));
+                if (wave_live) {
+                    acc_a = read_u(i0 + slot(0));
+#pragma unroll
+                    for (int j = 0; j < RK; ++j)
+                        acc_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(i0 + slot(0), j), xf[j], acc_a, 0, 0, 0);
+                }
+                release(i0 + slot(0));
+                int u = 0;
+                for (; u + 2 < nts; u += 2) {
+                    wait_ready(i0 + slot(u + 1));
+                    if (wave_live) pipelined(acc_a, acc_b, i0 + slot(u + 1), tile_of(slot(u)));
+                    release(i0 + slot(u + 1));
+                    wait_ready(i0 + slot(u + 2));
+                    if (wave_live) pipelined(acc_b, acc_a, i0 + slot(u + 2), tile_of(slot(u + 1)));
+                    release(i0 + slot(u + 2));
+                }
+                // one or two tiles left, the first in acc_a; only the segment's last slot can be the vocabulary's tail
+                const bool tail = slot(nts - 1) == ntw - 1 && tile_of(ntw - 1) == a.ntiles - 1 && a.ntiles * kRTileV > a.V;
+                if (u + 1 < nts) {
+                    wait_ready(i0 + slot(u + 1));
+                    if (wave_live) pipelined(acc_a, acc_b, i0 + slot(u + 1), tile_of(slot(u)));
+                    release(i0 + slot(u + 1));
+                    if (wave_live) {
+                        if (tail) last(acc_b, tile_of(slot(u + 1)), kMasked);
+                        else last(acc_b, tile_of(slot(u + 1)), kUnmasked);
+                    }
+                } else {
+                    if (wave_live) {
+                        if (tail) last(acc_a, tile_of(slot(u)), kMasked);
+                        else last(acc_a, tile_of(slot(u)), kUnmasked);
+                    }
+                }
             }
         }
 
-        // end of this position / row block: lane merge, global pick, log-sum-exp partials
-        if (wave_live) {
+        // end of this position / row block: lane merge, merge of the sets, global pick, log-sum-exp partials.
+        // With several sets every consumer wave takes part in the hand-over (a set without tiles carries neutral
+        // values), so the hand-over counters stay in step.
+        if (SETS > 1 || wave_live) {
             int bi = (btile >= 0) ? 32 * btile + 16 * half + bslot : 0x7FFFFFFF;
             float key, lbest;
             if (SAMPLE) {
@@ -767,9 +857,63 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 lbest = ol;
             }
             lse_merge(mc2, s2, omc, os);
+            if constexpr (SETS > 1) {
+                // sets 1 .. SETS-1 hand over; set 0 merges them in set order
+                const int mb = seg & 1;
+                if (cset > 0) {
+                    const int h = cset - 1;
+                    uint32_t spins = 0;
+                    while (lds_load(&mgot[h][wrow]) + 1u < (uint32_t)seg) {  // set 0 has read this buffer's last use
+                        __builtin_amdgcn_s_sleep(0);
+                        if (++spins > spin_limit) {
+                            __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
+                    if (half == 0) {
+                        float* q = &mx[mb][h][wrow][0][rho];
+                        q[0] = key;
+                        q[32] = __int_as_float(bi);
+                        q[64] = lbest;
+                        q[96] = mc2;
+                        q[128] = s2;
+                    }
+                    wait_lgkmcnt0();
+                    __asm__ volatile("" ::: "memory");
+                    if (lane == 0) lds_add(&mput[h][wrow], 1u);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < SETS - 1; ++h) {
+                        uint32_t spins = 0;
+                        while (lds_load(&mput[h][wrow]) < (uint32_t)(seg + 1)) {
+                            __builtin_amdgcn_s_sleep(0);
+                            if (++spins > spin_limit) {
+                                __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                break;
+                            }
+                        }
+                        __asm__ volatile("" ::: "memory");
+                        const float* q = &mx[mb][h][wrow][0][rho];
+                        const float okey2 = q[0];
+                        const int oi2 = __float_as_int(q[32]);
+                        const float ol2 = q[64];
+                        const float omc2 = q[96];
+                        const float os2 = q[128];
+                        wait_lgkmcnt0();
+                        __asm__ volatile("" ::: "memory");
+                        if (lane == 0) lds_add(&mgot[h][wrow], 1u);
+                        if (beats(okey2, oi2, key, bi)) {
+                            key = okey2;
+                            bi = oi2;
+                            lbest = ol2;
+                        }
+                        lse_merge(mc2, s2, omc2, os2);
+                    }
+                }
+            }
             // the winner words and counters of this launch are cleared before the first atomics touch them
-            if (seg == 0 && lane == 0) wait_cleared(a, tag);
-            if (half == 0 && valid_b) {
+            if (cset == 0 && seg == 0 && lane == 0) wait_cleared(a, tag);
+            if (cset == 0 && half == 0 && valid_b) {
                 const unsigned long long packed =
                     ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
                 atomicMax(a.winners + (((size_t)k * a.Bpad + b) * kWinnerSlots + g % kWinnerSlots) * kWinnerStride, packed);
@@ -781,13 +925,13 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 agent_store(a.p_l + o, lbest);
             }
         }
-        if (rb == nrb - 1) {
+        if (rb == nrb - 1 && cset == 0) {
             // this wave's picks of position k are performed once its memory operations have completed
             wait_vmcnt<0>();
             int last_all = 0;
             if (lane == 0) {
                 const uint32_t prev = __hip_atomic_fetch_add(&stepdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (prev == (uint32_t)kConsumers * (uint32_t)(k + 1) - 1u)  // last consumer wave of the workgroup
+                if (prev == (uint32_t)kRowWaves * (uint32_t)(k + 1) - 1u)  // last set-0 wave of the workgroup
                     last_all = arrive(a, k) ? 1 : 0;
             }
             // the grid's last arrival writes every copy of the release word
@@ -811,69 +955,49 @@ hipError_t launch_confidence(const ConfArgs& c, int B, hipStream_t st) {
 
 int round_supported_r(int r) { return mfma_supported_r(r) && r <= 256; }
 
-int round_lds_bytes(int r) {
-    switch (r / 16) {
-        case 1: return Ring<1>::kNS * Ring<1>::kStage;
-        case 2: return Ring<2>::kNS * Ring<2>::kStage;
-        case 4: return Ring<4>::kNS * Ring<4>::kStage;
-        case 8: return Ring<8>::kNS * Ring<8>::kStage;
-        case 16: return Ring<16>::kNS * Ring<16>::kStage;
-        default: return 0;
-    }
+
+template <int RK, int MODE, bool GATED, int UR>
+static const void* round_fn() {
+    return reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED, UR>);
 }
 
 template <int RK, int MODE, bool GATED>
-static hipError_t coop_launch(const RoundArgs& a, hipStream_t st) {
-    RoundArgs copy = a;
-    void* args[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED>), dim3(a.G),
-                                      dim3(kRoundThreads), args, 0, st);
+static const void* round_fn(bool small) {
+    return small ? round_fn<RK, MODE, GATED, 1>() : round_fn<RK, MODE, GATED, 16>();
 }
 
 template <int RK>
-static hipError_t launch_round_rk(const RoundArgs& a, bool sample, bool gated, hipStream_t st) {
-    if (sample) return gated ? coop_launch<RK, kModeSample, true>(a, st) : coop_launch<RK, kModeSample, false>(a, st);
-    return gated ? coop_launch<RK, kModeGreedy, true>(a, st) : coop_launch<RK, kModeGreedy, false>(a, st);
+static const void* round_fn(bool sample, bool gated, bool small) {
+    if (sample) return gated ? round_fn<RK, kModeSample, true>(small) : round_fn<RK, kModeSample, false>(small);
+    return gated ? round_fn<RK, kModeGreedy, true>(small) : round_fn<RK, kModeGreedy, false>(small);
 }
 
-template <int RK, int MODE, bool GATED>
-static int max_blocks_per_cu() {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED>),
-                                                     kRoundThreads, 0) != hipSuccess)
-        return 0;
-    return n;
-}
-
-int round_max_coresident(int r, bool sample, bool gated) {
-    int per_cu = 0;
-#define DSPARK_OCC(RK_)                                                                                  \
-    per_cu = sample ? (gated ? max_blocks_per_cu<RK_, kModeSample, true>() : max_blocks_per_cu<RK_, kModeSample, false>()) \
-                    : (gated ? max_blocks_per_cu<RK_, kModeGreedy, true>() : max_blocks_per_cu<RK_, kModeGreedy, false>())
+static const void* round_fn_r(int r, bool sample, bool gated, bool small) {
     switch (r / 16) {
-        case 1: DSPARK_OCC(1); break;
-        case 2: DSPARK_OCC(2); break;
-        case 4: DSPARK_OCC(4); break;
-        case 8: DSPARK_OCC(8); break;
-        case 16: DSPARK_OCC(16); break;
-        default: return 0;
+        case 1: return round_fn<1>(sample, gated, small);
+        case 2: return round_fn<2>(sample, gated, small);
+        case 4: return round_fn<4>(sample, gated, small);
+        case 8: return round_fn<8>(sample, gated, small);
+        case 16: return round_fn<16>(sample, gated, small);
+        default: return nullptr;
     }
-#undef DSPARK_OCC
+}
+
+int round_max_coresident(int r, bool sample, bool gated, bool small) {
+    const void* fn = round_fn_r(r, sample, gated, small);
+    int per_cu = 0;
+    if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kRoundThreads, 0) != hipSuccess) return 0;
     return per_cu * device_cu_count();
 }
 
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
                                hipEvent_t ev_end) {
+    const void* fn = round_fn_r(a.r, sample, gated, round_small_block(a.B));
+    if (!fn) return hipErrorInvalidValue;
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
-    hipError_t e;
-    switch (a.r / 16) {
-        case 1: e = launch_round_rk<1>(a, sample, gated, st); break;
-        case 2: e = launch_round_rk<2>(a, sample, gated, st); break;
-        case 4: e = launch_round_rk<4>(a, sample, gated, st); break;
-        case 8: e = launch_round_rk<8>(a, sample, gated, st); break;
-        case 16: e = launch_round_rk<16>(a, sample, gated, st); break;
-        default: return hipErrorInvalidValue;
-    }
+    RoundArgs copy = a;
+    void* args[] = {&copy};
+    const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st);
     if (ev_end) (void)hipEventRecord(ev_end, st);
     return e;
 }

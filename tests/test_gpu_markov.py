@@ -33,6 +33,9 @@ def _rand_H(B, K, r, seed=0):
 # drafts with the persistent whole-round kernel; V % 4 != 0 with the per-position kernels; r=24 and r=48 and
 # fp32 weights take the vector-ALU path
 SHAPES = [
+    (8, 3, 3000, 256, S.BF16),   # the largest small block (at most 8 rows), ragged vocabulary tail
+    (2, 2, 2050, 128, S.BF16),
+    (9, 2, 1000, 256, S.BF16),   # the smallest batch on the full 128-row block
     (1, 4, 512, 16, S.F32),
     (3, 3, 1000, 16, S.BF16),
     (130, 2, 776, 32, S.BF16),
