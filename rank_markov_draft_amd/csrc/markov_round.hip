@@ -35,6 +35,12 @@
 //  * A ninth wave per workgroup (the finalizer) clears the pick words and counters at the start of the launch
 //    and, one position behind, merges the log-sum-exp partials of its rows into tokens and log-probabilities,
 //    so a round is a single launch.
+//  * A batch of at most 8 rows takes a small-block form: one U unit per item instead of sixteen, so the
+//    producers keep six items in flight and the ring has eight stages (a stream of W2-only items is bound by
+//    the bytes in flight), and with greedy picks the four consumer waves each take every fourth tile of a
+//    position for the same rows, handing their per-row results to wave 0 through LDS.
+//  * The gated gather X = bf16(W1[a] (.) H) runs in four phases whose loads are all issued before their
+//    multiplies, so it costs the pick read and four memory round trips.
 #include <type_traits>
 
 #include "common.hpp"
