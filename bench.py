@@ -85,7 +85,7 @@ def write_traffic(fetch_csv, write_csv):
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         d = per_kernel(path, counter)
         copy = max(d["__amd_rocclr_copyBuffer"])
-        kern = [v for k, v in d.items() if "markov_round_kernel<16, 1, false>" in k][0]
+        kern = [v for k, v in d.items() if "markov_round_kernel<16, 1, false, 16>" in k][0]
         mean = sum(kern) / len(kern)
         scale = gib_kib / copy
         rec[key] = {"counter": counter, "kib_per_launch": round(mean, 1), "launches": len(kern),
