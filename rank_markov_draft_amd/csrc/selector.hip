@@ -526,6 +526,90 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
     }
 }
 
+// The walk with every step's choice made in parallel.  A step's pick depends on the path only through the row
+// of the pair table it reads (the slot picked one step before); the row's keys (the scores, or the scores over T
+// plus the Gumbel noise of row b, step t and candidate id) and its log-sum-exp do not.  So the threads of the
+// workgroup take the table rows (the anchor row, then the topk rows of each later table) one per thread, and
+// record each row's pick (slot, id, exact log-probability); one thread then follows the path, one LDS read per
+// step.  This replaces sixteen dependent cross-lane reductions by one pass over the rows.  Rows are staged with
+// a pitch of topk + 1 floats, so that the threads' reads of the same column fall in distinct banks.
+constexpr int kWalkThreads = 256;
+
+size_t walk_rows_lds_bytes(int K, int topk) {
+    const size_t rows = 1 + (size_t)(K - 1) * topk;
+    return 4 * (rows * (topk + 1) + (size_t)K * topk + 3 * rows);
+}
+
+__global__ void __launch_bounds__(kWalkThreads) walk_rows_kernel(SelectorArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float wsh[];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int kk = a.topk, pitch = kk + 1;
+    const int rows = 1 + (a.K - 1) * kk;
+    const int tstride = kk + (a.K - 1) * kk * kk;
+    const float* sc = a.scores + (size_t)b * tstride;
+    const int32_t* cands = a.cand + (size_t)b * a.K * kk;
+    float* ss = wsh;                                                          // [rows][pitch]
+    int32_t* cs = reinterpret_cast<int32_t*>(ss + (size_t)rows * pitch);      // [K][topk] candidate ids
+    int32_t* pslot = cs + a.K * kk;                                           // per row: slot of its pick,
+    int32_t* pid = pslot + rows;                                              // its id,
+    float* plp = reinterpret_cast<float*>(pid + rows);                        // its log-probability
+
+    // stage (one round trip: every thread's loads are issued before its LDS writes)
+    constexpr int kBatch = 16;
+    for (int e0 = 0; e0 < tstride; e0 += kBatch * kWalkThreads) {
+        float v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int e = e0 + q * kWalkThreads + tid;
+            v[q] = e < tstride ? sc[e] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int e = e0 + q * kWalkThreads + tid;
+            if (e < tstride) ss[(e / kk) * pitch + e % kk] = v[q];
+        }
+    }
+    for (int e = tid; e < a.K * kk; e += kWalkThreads) cs[e] = cands[e];
+    __syncthreads();
+
+    for (int row = tid; row < rows; row += kWalkThreads) {
+        const int t = row == 0 ? 0 : 1 + (row - 1) / kk;  // the step whose choice this row makes
+        const float* rp = ss + (size_t)row * pitch;
+        const int32_t* ct = cs + t * kk;
+        const uint32_t k2 = a.sample ? noise_key2(a.k0, (uint32_t)b, (uint32_t)t) : 0u;
+        float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
+        int bi = 0x7FFFFFFF, bs = 0;
+        for (int j = 0; j < kk; ++j) {
+            const float l = rp[j];
+            const int c = ct[j];
+            const float tt = l * a.inv_t * kLog2e;
+            const float key = a.sample ? tt + gumbel_log2_units(fmix32(k2 ^ (uint32_t)c)) : l;
+            if (beats(key, c, bk, bi)) {
+                bk = key;
+                bi = c;
+                bl = l;
+                bs = j;
+            }
+            lse_merge(m, s, tt, 1.0f);
+        }
+        pslot[row] = bs;
+        pid[row] = bi;
+        plp[row] = bl * a.inv_t - (m + fast_log2(s)) * kLn2;
+    }
+    __syncthreads();
+
+    if (tid == 0) {
+        int islot = 0;
+        for (int t = 0; t < a.K; ++t) {
+            const int row = (t == 0) ? 0 : 1 + (t - 1) * kk + islot;
+            a.tokens[(size_t)b * a.K + t] = pid[row];
+            if (a.logprobs) a.logprobs[(size_t)b * a.K + t] = plp[row];
+            islot = pslot[row];
+        }
+    }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int, int, int) { return 0; }
@@ -568,8 +652,12 @@ hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_walk(const SelectorArgs& a, hipStream_t st) {
+    // rows resolved in parallel when the padded tables fit 64 KB of LDS; else one step at a time, from LDS
+    // copies of the tables or, for the largest tables, from global memory
+    const size_t rows_lds = walk_rows_lds_bytes(a.K, a.topk);
     const size_t lds = sizeof(float) * (a.topk + (size_t)(a.K - 1) * a.topk * a.topk + (size_t)a.K * a.topk);
-    if (lds <= 64 * 1024) hipLaunchKernelGGL(walk_kernel<true>, dim3(a.B), dim3(64), lds, st, a);
+    if (rows_lds <= 64 * 1024) hipLaunchKernelGGL(walk_rows_kernel, dim3(a.B), dim3(kWalkThreads), rows_lds, st, a);
+    else if (lds <= 64 * 1024) hipLaunchKernelGGL(walk_kernel<true>, dim3(a.B), dim3(64), lds, st, a);
     else hipLaunchKernelGGL(walk_kernel<false>, dim3(a.B), dim3(64), 0, st, a);
     return hipGetLastError();
 }

@@ -50,7 +50,9 @@ def test_topk_large_k_small_vocab(D, V, k):
 
 SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 96, 16, 16, S.F32),
               (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16), (3, 3, 2000, 32, 32, S.BF16),
-              (2, 3, 5000, 64, 64, S.BF16)]
+              (2, 3, 5000, 64, 64, S.BF16),
+              # K = 16 with k = 32 and 64: tables beyond the row-parallel walk's LDS, walked step by step
+              (2, 16, 1000, 32, 32, S.BF16), (2, 16, 1000, 32, 64, S.BF16)]
 
 
 @pytest.mark.parametrize("shape", SEL_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d-k%d" % s[:5])
