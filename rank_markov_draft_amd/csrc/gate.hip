@@ -13,8 +13,9 @@
 // The product is small (one workgroup per output tile: 256 at 1024 rows x r = 256) and each step waits on
 // memory, so the k range is split eight ways: two waves per SIMD hide each other's waits and each wave's
 // chain is short (at rows = 1024, D = 4096, r = 256, event-timed with launch: 21.7 us with four waves, 17.6
-// with eight, 20.0 with sixteen).  What remains is the tiling: the 32 x 32 tiles re-read h once per column
-// block and Wg once per row block, about 128 MB of L2 reads for 10.5 MB of operands.
+// with eight, 20.0 with sixteen; four k steps of loads in flight per wave instead of one: 19.5).  What remains
+// is the tiling: the 32 x 32 tiles re-read h once per column block and Wg once per row block, about 128 MB
+// of L2 reads for 10.5 MB of operands.
 #include "internal.hpp"
 
 namespace dspark {
