@@ -232,11 +232,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     using RG = Ring<RK, UR>;
     constexpr bool SAMPLE = MODE == kModeSample;
     // Consumer sets: a small block (at most 8 rows) leaves three of the four consumer waves without rows, so
-    // with greedy picks each wave instead forms a set of its own on the same 32 rows and takes every fourth tile
-    // of a position (slots s, s + 4, ...), handing its per-row results to set 0 through LDS at the end of the
-    // position.  Sampling and the gate keep one set: the sampling epilogue and the gated gather hold more
-    // registers, and with the hand-over code the kernel would spill at three waves per SIMD.
-    constexpr int SETS = (UR == 1 && !SAMPLE && !GATED) ? 4 : 1;
+    // each wave instead forms a set of its own on the same 32 rows and takes every fourth tile of a position
+    // (slots s, s + 4, ...), handing its per-row results to set 0 through LDS at the end of the position (the
+    // greedy maximum and the block race are both maxima over tiles, merged in set order).  The gate keeps one
+    // set: the gated gather holds more registers, and with the hand-over code the kernel would spill at three
+    // waves per SIMD.
+    constexpr int SETS = (UR == 1 && !GATED) ? 4 : 1;
     constexpr int kRowWaves = kConsumers / SETS;  // consumer waves of one set (32 rows each)
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kNS * RG::kStage];
     __shared__ uint32_t ready[RG::kNS];  // +1 per producer per filled stage
