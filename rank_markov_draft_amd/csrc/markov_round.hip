@@ -37,7 +37,7 @@
 //    so a round is a single launch.
 //  * A batch of at most 8 rows takes a small-block form: one U unit per item instead of sixteen, so the
 //    producers keep six items in flight and the ring has eight stages (a stream of W2-only items is bound by
-//    the bytes in flight), and with greedy picks the four consumer waves each take every fourth tile of a
+//    the bytes in flight), and (without the gate) the four consumer waves each take every fourth tile of a
 //    position for the same rows, handing their per-row results to wave 0 through LDS.
 //  * The gated gather X = bf16(W1[a] (.) H) runs in four phases whose loads are all issued before their
 //    multiplies, so it costs the pick read and four memory round trips.
