@@ -85,9 +85,10 @@ def test_draft_parity(D, shape, mode, strength):
     check_draft(tok, lp, ref, what=f"{shape} {mode} {strength}")
 
 
+@pytest.mark.parametrize("B,V", [(9, 900), (4, 20000)], ids=["B9", "B4-small-block"])
 @pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
-def test_draft_gated_and_rv_layout(D, mode):
-    w = S.strong("gated", B=9, K=4, V=900, r=64, D=0, mode=mode)
+def test_draft_gated_and_rv_layout(D, mode, B, V):
+    w = S.strong("gated", B=B, K=4, V=V, r=64, D=0, mode=mode)
     H = _rand_H(w.B, w.K, w.r, seed=3)
     tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2), t_i32(w.anchor), w2_layout=D.DSPARK_W2_RV,
                                     H=t_f32(H), mode=mode, seed=11)
@@ -97,6 +98,9 @@ def test_draft_gated_and_rv_layout(D, mode):
 
 
 def test_gate_ones_equals_ungated_bitwise(D):
+    """H = 1 makes X = W1[a] exactly.  At this size every workgroup holds one vocabulary tile, so the gated and
+    ungated small-block forms (one consumer set against four) also merge their log-sum-exp terms in the same
+    order and the log-probabilities agree bit for bit; with several tiles per workgroup the tokens still do."""
     w = S.strong("serving", B=6, K=3, V=700, r=64, mode=S.SAMPLE)
     a = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), mode=D.DSPARK_SAMPLE, seed=5)
     b = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), mode=D.DSPARK_SAMPLE, seed=5,
