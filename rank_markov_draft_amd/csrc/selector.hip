@@ -441,46 +441,14 @@ __global__ void __launch_bounds__(256) pair_score_mfma_kernel(SelectorArgs a) {
     }
 }
 
-// One wave per row: K serial picks.  STAGED: the row's score tables and candidate ids are first copied to
-// LDS with independent loads, so the serial chain runs on LDS latency instead of memory latency.
-template <bool STAGED>
+// One wave per row: K serial picks, reading the row's score tables and candidate ids from global memory (the
+// tables too large for the row-parallel walk below even with all of a workgroup's LDS).
 __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
-    extern __shared__ __attribute__((aligned(16))) float wsh[];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const size_t tstride = a.topk + (size_t)(a.K - 1) * a.topk * a.topk;
     const float* sc = a.scores + (size_t)b * tstride;
     const int32_t* cands = a.cand + (size_t)b * a.K * a.topk;
-    if (STAGED) {
-        float* ss = wsh;
-        int32_t* cs = reinterpret_cast<int32_t*>(wsh + tstride);
-        const int nc = a.K * a.topk;
-        // the copy is one round trip: 16-byte loads, up to 16 per lane in flight
-        constexpr int kBatch = 16;
-        const int n4 = ((uintptr_t)sc % 16 == 0) ? (int)(tstride / 4) : 0;
-        const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(sc);
-        f32x4_t* d4 = reinterpret_cast<f32x4_t*>(ss);
-        for (int i0 = 0; i0 < n4; i0 += 64 * kBatch) {
-            f32x4_t v[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int i = i0 + 64 * q + lane;
-                v[q] = i < n4 ? s4[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int i = i0 + 64 * q + lane;
-                if (i < n4) d4[i] = v[q];
-            }
-        }
-#pragma unroll 8
-        for (int i = 4 * n4 + lane; i < (int)tstride; i += 64) ss[i] = sc[i];
-#pragma unroll 4
-        for (int i = lane; i < nc; i += 64) cs[i] = cands[i];
-        __syncthreads();
-        sc = ss;
-        cands = cs;
-    }
     int islot = 0;
     for (int t = 0; t < a.K; ++t) {
         const float* rowp = (t == 0) ? sc : sc + a.topk + ((size_t)(t - 1) * a.topk + islot) * a.topk;
@@ -534,6 +502,7 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
 // step.  This replaces sixteen dependent cross-lane reductions by one pass over the rows.  Rows are staged with
 // a pitch of topk + 1 floats, so that the threads' reads of the same column fall in distinct banks.
 constexpr int kWalkThreads = 256;
+constexpr int kWalkLdsMax = 160 * 1024;  // a workgroup's LDS on gfx950
 
 size_t walk_rows_lds_bytes(int K, int topk) {
     const size_t rows = 1 + (size_t)(K - 1) * topk;
@@ -652,13 +621,15 @@ hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_walk(const SelectorArgs& a, hipStream_t st) {
-    // rows resolved in parallel when the padded tables fit 64 KB of LDS; else one step at a time, from LDS
-    // copies of the tables or, for the largest tables, from global memory
+    // Rows resolved in parallel when the padded tables fit the workgroup's LDS (160 KB on this part: top-16 and
+    // top-32 at K = 16); else one step at a time from global memory (top-64 at K = 16).
+    static const size_t rows_cap = hipFuncSetAttribute(reinterpret_cast<const void*>(&walk_rows_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWalkLdsMax) == hipSuccess
+                                       ? (size_t)kWalkLdsMax
+                                       : (size_t)64 * 1024;
     const size_t rows_lds = walk_rows_lds_bytes(a.K, a.topk);
-    const size_t lds = sizeof(float) * (a.topk + (size_t)(a.K - 1) * a.topk * a.topk + (size_t)a.K * a.topk);
-    if (rows_lds <= 64 * 1024) hipLaunchKernelGGL(walk_rows_kernel, dim3(a.B), dim3(kWalkThreads), rows_lds, st, a);
-    else if (lds <= 64 * 1024) hipLaunchKernelGGL(walk_kernel<true>, dim3(a.B), dim3(64), lds, st, a);
-    else hipLaunchKernelGGL(walk_kernel<false>, dim3(a.B), dim3(64), 0, st, a);
+    if (rows_lds <= rows_cap) hipLaunchKernelGGL(walk_rows_kernel, dim3(a.B), dim3(kWalkThreads), rows_lds, st, a);
+    else hipLaunchKernelGGL(walk_kernel, dim3(a.B), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

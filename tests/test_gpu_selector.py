@@ -51,7 +51,8 @@ def test_topk_large_k_small_vocab(D, V, k):
 SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 96, 16, 16, S.F32),
               (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16), (3, 3, 2000, 32, 32, S.BF16),
               (2, 3, 5000, 64, 64, S.BF16),
-              # K = 16 with k = 32 and 64: tables beyond the row-parallel walk's LDS, walked step by step
+              # K = 16 with k = 32 (the row-parallel walk with more than 64 KB of LDS) and k = 64 (tables
+              # beyond the workgroup's LDS, walked step by step from global memory)
               (2, 16, 1000, 32, 32, S.BF16), (2, 16, 1000, 32, 64, S.BF16)]
 
 
