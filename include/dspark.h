@@ -38,12 +38,15 @@
  * from a counter hash: fmix(x) is the MurmurHash3 32-bit finalisation mix (A. Appleby, public domain);
  * k0 = fmix(lo32(seed) ^ fmix(hi32(seed))), k1 = fmix(k0 ^ b), k2 = fmix(k1 ^ k), h(n) = fmix(k2 ^ n);
  * u(n) = (2 * (h(n) >> 9) + 1) / 2^24.  b is the batch row, k the draft position (0-based).
- *  - Whole-vocabulary draws (the Markov head) race aligned blocks of 16 ids: with p_v = exp(l_v / T - M),
- *    block j (ids 16 j .. 16 j + 15) has mass S_j = sum of its p_v and variate E_j = -ln u(2 j); the block
- *    with the largest S_j / E_j wins, and the drawn id is the first in it whose inclusive prefix mass
- *    exceeds u(2 j + 1) S_j.  An exact draw from softmax(l / T).
- *  - Restricted candidate sets (the Selector's walk) use Gumbel-max: argmax over the candidates of
- *    l_v / T + G(v), G(v) = -ln(-ln u(v)) with n = v the vocabulary id (never a candidate slot).
+ *  - A draw over a set of ids (the whole vocabulary for the Markov head, the candidate set for the Selector's
+ *    walk) races the set's members grouped in aligned vocabulary blocks of 16 ids: with p_v = exp(l_v / T - M),
+ *    block j (ids 16 j .. 16 j + 15 that belong to the set) has mass S_j = sum of its members' p_v and variate
+ *    E_j = -ln u(2 j); the block with the largest S_j / E_j wins (equivalently the largest ln S_j + G_j with
+ *    G_j = -ln(-ln u(2 j)) a Gumbel variate: a Gumbel-max over blocks; ties to the lower block), and the drawn
+ *    id is the first member of the winner, in ascending id order, whose inclusive prefix mass exceeds
+ *    u(2 j + 1) S_j.  An exact draw from softmax(l / T) over the set, one hash pair per block rather than one
+ *    hash per id; the noise keys on vocabulary blocks, never on candidate slots, so a candidate set holding
+ *    the whole vocabulary draws exactly what the full head draws.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -112,11 +115,42 @@ size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int
  * mode     DSPARK_GREEDY or DSPARK_SAMPLE; seed and temperature (> 0) are used in SAMPLE mode only.
  * tokens   [B, K] int32 output.   logprobs: [B, K] fp32 output or NULL.
  * Accumulation is fp32 over bf16 (or fp32) products; the gated bf16 path rounds x to bf16 (nearest even).
+ * Device-side failure: the whole-round kernel (one persistent launch per call) waits on other workgroups with
+ * bounded spins.  If a wait gives up (it never should on an idle device; a device shared with other work that
+ * keeps workgroups from being co-resident could cause it), the kernel still exits normally, writes tokens = -1
+ * and logprobs = NaN at the positions it could not finish and sets an error word in the workspace; the call
+ * itself has already returned DSPARK_OK.  Callers that must not feed -1 onward check dspark_markov_status.
  */
 int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
                         const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
                         uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Device-side status of the last dspark_markov_draft* call made with this workspace (and these B, K) on
+ * `stream`: waits for the stream (this call synchronises the host), then returns DSPARK_EDEVICE if a bounded
+ * wait of the whole-round kernel gave up (tokens -1 and logprobs NaN where it failed), DSPARK_OK otherwise.
+ */
+int dspark_markov_status(const void* workspace, size_t workspace_bytes, int B, int K, void* stream);
+
+/*
+ * Testing hook: the number of sleeps after which a bounded wait of the whole-round kernel gives up, for the
+ * calls that follow in this process (0 restores the default, 2^22).  A tiny limit forces the failure path of
+ * dspark_markov_status without faulting: every wait still ends and the kernel exits normally.
+ */
+void dspark_set_spin_limit(uint32_t sleeps);
+
+/*
+ * Validation call: dspark_markov_draft (same arguments and results) that also writes the calibrated logits of
+ * every position along the drafted path, logits[b, k, v] = l[v] with a_k = tokens[b, k-1] (fp32, [B, K, V]),
+ * computed by the drafting kernel itself (the whole-round kernel with a store epilogue: the same contraction and
+ * the same pick).  Only shapes that take the whole-round kernel (bf16 weights, r % 16 == 0, r <= 256,
+ * V % 4 == 0, 16-byte aligned buffers) are accepted; DSPARK_EUNSUPPORTED otherwise.
+ */
+int dspark_markov_draft_logits(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                               const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                               uint64_t seed, float temperature, int32_t* tokens, float* logprobs, float* logits,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dspark_markov_draft plus the confidence head and prefix survival of the drafted block (DSpark overview,
@@ -241,10 +275,10 @@ size_t dspark_selector_workspace_bytes(int B, int K, int V, int r, int topk);
  *  2. pair scores, all in parallel: the anchor row  S0[b, j] = U[b,0,c_0j] + < A[anchor_b] (.) H[b,0], Bemb[c_0j] >
  *     and for t >= 1  S_t[b, i, j] = U[b,t,c_tj] + < A[c_{t-1,i}] (.) H[b,t], Bemb[c_tj] >;
  *  3. the walk: i_0 = pick over S0[b, :], i_t = pick over S_t[b, i_{t-1}, :]; tokens[b, t] = c_{t, i_t}.
- *     The pick over the k candidates is the argmax (GREEDY) or Gumbel-max keyed on vocabulary ids
- *     (SAMPLE; see Noise); logprobs[b, t] = log softmax over the walked row of scores / T.
+ *     The pick over the k candidates is the argmax (GREEDY) or the draw of Noise restricted to the
+ *     candidates (SAMPLE); logprobs[b, t] = log softmax over the walked row of scores / T.
  * U [B, K, V] fp32; A, Bemb [V, r] of type wdtype; anchor [B]; H [B, K, r] fp32 or NULL.
- * topk as for dspark_topk; r <= 1024 (rows are staged with 16-byte loads when r % 8 == 0 for bf16 or
+ * topk as for dspark_topk and at most 1024 (DSPARK_EUNSUPPORTED above); r <= 1024 (rows are staged with 16-byte loads when r % 8 == 0 for bf16 or
  * r % 4 == 0 for fp32 and A, Bemb are 16-byte aligned, element by element otherwise).
  * tokens [B, K] int32 output; logprobs [B, K] fp32 or NULL; cand [B, K, topk] int32 or NULL;
  * scores [B, topk + (K-1) * topk * topk] fp32 or NULL (anchor row, then the K-1 tables, row-major i, j).

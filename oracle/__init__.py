@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB_PATH lets the mutation tests load a deliberately broken copy in a child process
+_LIB_PATH = os.environ.get("ORACLE_LIB_PATH") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16 = 0, 1
@@ -48,11 +49,11 @@ def _load():
         lib.oracle_schedule_best.argtypes = [vp, vp, i32, i32, vp]
         lib.oracle_schedule_best.restype = dbl
         lib.oracle_markov_draft.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, dbl,
-                                            vp, vp, i32, vp, vp, vp, vp, vp]
+                                            vp, vp, i32, vp, vp, vp, vp, vp, vp, dbl]
         lib.oracle_markov_logits.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp]
         lib.oracle_topk.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         lib.oracle_markov_restricted.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                                 u64, dbl, vp, i32, vp, vp, vp]
+                                                 u64, dbl, vp, vp, i32, vp, vp, vp, vp, vp, dbl]
         lib.oracle_selector_draft.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, u64, dbl,
                                               vp, i32, vp, vp, vp, vp, vp]
         lib.oracle_enumerate_paths.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, i32, dbl, vp]
@@ -177,11 +178,15 @@ def schedule_best(a, sps):
 
 # -------------------------------------------------------------------------------------------- markov
 
+REACH_EPS = 1e-2  # perturbation of every key / log-mass under which a differing token is still accepted
+
+
 def markov_draft(U, W1, W2, anchor, *, w2_layout=W2_RV, H=None, mode=GREEDY, seed=0, temperature=1.0,
-                 follow=None, rows=None):
+                 follow=None, rows=None, eps=REACH_EPS):
     """Full-vocabulary Markov head over K positions (fp64).  Returns a dict of [B,K] arrays:
-    tokens, logprobs, margins, best_logit, and lp_follow when ``follow`` is given.  Rows not listed in
-    ``rows`` are left as -1 / nan."""
+    tokens, logprobs, margins, best_logit, and lp_follow and reach when ``follow`` is given (reach: the
+    follow token is the pick, or a perturbation of at most ``eps`` of every key selects it).  Rows not
+    listed in ``rows`` are left as -1 / nan."""
     U = _c(U, np.float32)
     B, K, V = U.shape
     W1, wd = _w(W1)
@@ -197,12 +202,14 @@ def markov_draft(U, W1, W2, anchor, *, w2_layout=W2_RV, H=None, mode=GREEDY, see
     mg = np.full((B, K), np.nan)
     bl = np.full((B, K), np.nan)
     lpf = np.full((B, K), np.nan) if follow is not None else None
+    reach = np.full((B, K), -1, np.int32) if follow is not None else None
     _load().oracle_markov_draft(_ptr(U), _ptr(W1), _ptr(W2), wd, w2_layout, _ptr(anchor), _ptr(H), B, K, V, r,
                                 mode, seed, float(temperature), _ptr(follow), _ptr(rr), nr, _ptr(tokens), _ptr(lp),
-                                _ptr(mg), _ptr(lpf), _ptr(bl))
+                                _ptr(mg), _ptr(lpf), _ptr(bl), _ptr(reach), float(eps))
     out = dict(tokens=tokens, logprobs=lp, margins=mg, best_logit=bl)
     if lpf is not None:
         out["lp_follow"] = lpf
+        out["reach"] = reach
     return out
 
 
@@ -223,7 +230,8 @@ def markov_logits(Uk, W1, W2, prev, *, w2_layout=W2_RV, Hk=None, rows=None):
 
 
 def markov_restricted(U, W1, W2, anchor, cand, *, w2_layout=W2_RV, H=None, mode=GREEDY, seed=0,
-                      temperature=1.0, rows=None):
+                      temperature=1.0, follow=None, rows=None, eps=REACH_EPS):
+    """The head restricted to the candidate sets cand [B, K, topk] (fp64); outputs as markov_draft."""
     U = _c(U, np.float32)
     B, K, V = U.shape
     W1, wd = _w(W1)
@@ -233,14 +241,21 @@ def markov_restricted(U, W1, W2, anchor, cand, *, w2_layout=W2_RV, H=None, mode=
     topk = cand.shape[-1]
     anchor = _c(anchor, np.int32)
     H = _c(H, np.float64)
+    follow = _c(follow, np.int32)
     rr, nr = _rows(rows)
     tokens = np.full((B, K), -1, np.int32)
     lp = np.full((B, K), np.nan)
     mg = np.full((B, K), np.nan)
+    lpf = np.full((B, K), np.nan) if follow is not None else None
+    reach = np.full((B, K), -1, np.int32) if follow is not None else None
     _load().oracle_markov_restricted(_ptr(U), _ptr(W1), _ptr(W2), wd, w2_layout, _ptr(anchor), _ptr(H), _ptr(cand),
-                                     B, K, V, r, topk, mode, seed, float(temperature), _ptr(rr), nr, _ptr(tokens),
-                                     _ptr(lp), _ptr(mg))
-    return dict(tokens=tokens, logprobs=lp, margins=mg)
+                                     B, K, V, r, topk, mode, seed, float(temperature), _ptr(follow), _ptr(rr), nr,
+                                     _ptr(tokens), _ptr(lp), _ptr(mg), _ptr(lpf), _ptr(reach), float(eps))
+    out = dict(tokens=tokens, logprobs=lp, margins=mg)
+    if lpf is not None:
+        out["lp_follow"] = lpf
+        out["reach"] = reach
+    return out
 
 
 # ----------------------------------------------------------------------------------------- selector

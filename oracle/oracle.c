@@ -26,10 +26,11 @@
  * Readings where the pages leave a step open (each listed with its reason in the design notes):
  *  - position 1 is conditioned on the anchor token;
  *  - ties in every argmax / top-k go to the lower vocabulary id (never the candidate slot);
- *  - sampling a restricted candidate set (the Selector, the truncated head) is Gumbel-max at temperature
- *    T: key = l/T + G(seed,b,k,v); greedy ignores T;
- *  - sampling the whole vocabulary is an exact draw from softmax(l/T) by a two-level exponential race
- *    over aligned blocks of 16 ids (one race variate per block, then inverse CDF inside the winner);
+ *  - sampling is an exact draw from softmax(l/T) over the set the pick ranges over (the whole vocabulary,
+ *    or a candidate set) by one definition: a Gumbel-max race between the set's members grouped in aligned
+ *    vocabulary blocks of 16 ids (noise keyed on (seed, row, position, block)), then inverse CDF inside the
+ *    winning block; so a candidate set holding every id draws exactly what the whole vocabulary draws;
+ *    greedy ignores T;
  *  - the reported log-probability is log softmax(l/T)[token] over the same set the pick ranges over;
  *  - the gate multiplies the predecessor embedding: x = W1[a] (.) H(h_k).
  *
@@ -268,101 +269,218 @@ static double calibrated_logit(const float* Uk, const void* W2, int dtype, int l
     return (double)Uk[v] + bias;
 }
 
-/* Pick over a set of n logits l[0..n) whose vocabulary ids are ids[0..n) (ids == NULL: id = slot).
- * key = l (greedy) or l/T + G(seed,row,pos,id) (Gumbel-max, [DSp] "DSpark vs DFlash 2": sample from
- * the corrected logits).  Ties go to the lower vocabulary id.  Returns the slot picked; writes the
- * top-2 key margin and the log-softmax of l/T at the pick ([Tut] "Why the normalization has to be
- * local": the exact per-position probability of the drawn token). */
-static int pick(const double* l, const int32_t* ids, int n, int mode, uint64_t seed, int row, int pos,
-                double T, double* margin, double* logprob, double* lse_out) {
-    int best = -1;
-    double k1 = -INFINITY, k2 = -INFINITY;
-    for (int s = 0; s < n; ++s) {
-        int id = ids ? ids[s] : s;
-        double key = (mode == OR_SAMPLE) ? l[s] / T + oracle_gumbel(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)id) : l[s];
-        int better = (best < 0) || key > k1 || (key == k1 && id < (ids ? ids[best] : best));
-        if (better) {
-            if (best >= 0) k2 = k1;
-            k1 = key;
-            best = s;
-        } else if (key > k2) {
-            k2 = key;
-        }
+/* The pick at one position ranges over a set of n logits l[0..n) with distinct vocabulary ids ids[0..n)
+ * (ids == NULL: the whole vocabulary, id = slot).  Every sum over the set runs in ascending id order, so a
+ * candidate set that holds every id gives, bit for bit, what the whole vocabulary gives.
+ *
+ * Greedy: the largest l, ties to the lower id.
+ * Sampling ([DSp] "DSpark vs DFlash 2": sample from the corrected logits; the pages fix the distribution,
+ * softmax(l/T) over the set, not the sampler): a two-level exponential race.  With p_v = exp(l_v/T - M),
+ * M = max l/T, the members are grouped by vocabulary block q = id div 16 (aligned blocks of 16 ids; a
+ * restricted set may hold only some ids of a block).  Block q has mass S_q = sum of its members' p_v and race
+ * key ln S_q + G_q with G_q = -ln(-ln u(seed,row,pos, 2q)), a Gumbel variate of the counter hash: the block
+ * with the largest key wins (ties to the lower block), i.e. a Gumbel-max over blocks.  Inside the winner the
+ * id is the first member (ascending id) whose inclusive prefix mass exceeds u(seed,row,pos, 2q+1) S_q.  The
+ * arg-max of ln S_q + G_q is block q with probability S_q / sum S (Gumbel-max), and the inverse CDF then takes
+ * v with probability p_v / S_q: the draw is exactly softmax(l/T) over the set.
+ * Log-probability: l/T - LSE at the pick, LSE = M + ln sum_q S_q (greedy: T = 1) ([Tut] "Why the
+ * normalization has to be local": the exact probability of the drawn token).
+ *
+ * Margin (north star's "top-2 margin"; every term moves by at most 2 eps when each key l (greedy) or log-mass
+ * l/T (sampling) moves by at most eps): greedy, the gap between the two largest l; sampling, the smallest of
+ * the race gap between the two largest block keys and, inside the winner, the log-ratio margins of the two
+ * inverse-CDF comparisons: with A the mass before the drawn id, m its mass, C the mass after it and u the
+ * target uniform, ln(u (m + C)) - ln((1 - u) A) for "A <= u S" (A > 0) and ln((1 - u)(A + m)) - ln(u C) for
+ * "u S < A + m" (C > 0).
+ *
+ * Reachability of a given id f (the GPU's token, to be checked where it differs from the oracle's): f is
+ * reachable when some perturbation of every key / log-mass by at most eps makes the pick f.  Greedy:
+ * l_f >= max l - 2 eps.  Sampling: f's block could win the race (its key within 2 eps of the best other
+ * block's) and f's interval could hold the target: with A, m, C as above for f, the comparisons
+ * (1 - u) A' <= u (m' + C') and u C' < (1 - u)(A' + m') must hold together for some A' in [A e^-eps, A e^eps],
+ * C' in [C e^-eps, C e^eps], m' = m e^eps (both are conditions on z = (1 - u) A' - u C', which sweeps an
+ * interval).  The two levels are tested separately, which can only widen the accepted set. */
+typedef struct {
+    int32_t id;
+    int slot;
+} id_slot;
+
+static int by_id(const void* x, const void* y) {
+    const int32_t a = ((const id_slot*)x)->id, b = ((const id_slot*)y)->id;
+    return (a > b) - (a < b);
+}
+
+/* Slots of the set in ascending id order (ids == NULL: the identity). */
+static int* id_order(const int32_t* ids, int n) {
+    int* ord = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    if (!ids) {
+        for (int s = 0; s < n; ++s) ord[s] = s;
+        return ord;
     }
-    double Teff = (mode == OR_SAMPLE) ? T : 1.0;
+    id_slot* t = (id_slot*)malloc(sizeof(id_slot) * (size_t)(n > 0 ? n : 1));
+    for (int s = 0; s < n; ++s) {
+        t[s].id = ids[s];
+        t[s].slot = s;
+    }
+    qsort(t, (size_t)n, sizeof(id_slot), by_id);
+    for (int s = 0; s < n; ++s) ord[s] = t[s].slot;
+    free(t);
+    return ord;
+}
+
+#define ID_OF(s) (ids ? ids[(s)] : (s))
+
+/* Vocabulary block of an id in the sampling race: aligned blocks of 16 ids. */
+static int block_of(int32_t id) { return id / 16; }
+
+/* Result of one pick; reach is set only when a follow id is given (follow_id >= 0). */
+typedef struct {
+    int slot;          /* slot picked */
+    double margin;
+    double logprob;    /* log softmax at the pick */
+    double lse;
+    double lp_follow;  /* log softmax at the follow id (NaN if it is not in the set) */
+    int reach;         /* the follow id is the pick or reachable */
+} pick_out;
+
+static void choose(const double* l, const int32_t* ids, int n, int mode, uint64_t seed, int row, int pos, double T,
+                   int follow_id, double eps, pick_out* out) {
+    int* ord = id_order(ids, n);
+    const double Teff = (mode == OR_SAMPLE) ? T : 1.0;
     double M = -INFINITY;
     for (int s = 0; s < n; ++s)
         if (l[s] / Teff > M) M = l[s] / Teff;
-    double sum = 0.0;
-    for (int s = 0; s < n; ++s) sum += exp(l[s] / Teff - M);
-    double lse = M + log(sum);
-    if (margin) *margin = k1 - k2;
-    if (logprob) *logprob = l[best] / Teff - lse;
-    if (lse_out) *lse_out = lse;
-    return best;
+    /* the follow id's slot, if it is a member */
+    int fslot = -1;
+    for (int s = 0; s < n && follow_id >= 0; ++s)
+        if (ID_OF(s) == follow_id) fslot = s;
+    out->reach = 0;
+    out->lp_follow = NAN;
+    if (mode != OR_SAMPLE) {
+        int best = -1;
+        double k1 = -INFINITY, k2 = -INFINITY, total = 0.0;
+        for (int i = 0; i < n; ++i) {
+            const int s = ord[i];
+            total += exp(l[s] - M);
+            if (best < 0 || l[s] > k1) { /* ascending ids: an equal key keeps the lower id */
+                if (best >= 0) k2 = k1;
+                k1 = l[s];
+                best = s;
+            } else if (l[s] > k2) {
+                k2 = l[s];
+            }
+        }
+        out->slot = best;
+        out->margin = k1 - k2;
+        out->lse = M + log(total);
+        out->logprob = l[best] - out->lse;
+        if (fslot >= 0) {
+            out->lp_follow = l[fslot] - out->lse;
+            out->reach = (fslot == best) || (l[fslot] >= k1 - 2.0 * eps);
+        }
+        free(ord);
+        return;
+    }
+    /* sampling: blocks are runs of equal id / 16 in id order */
+    double total = 0.0, k1 = -INFINITY, k2 = -INFINITY;
+    int J = -1;     /* winning block */
+    int Jbeg = 0, Jend = 0;
+    double SJ = 0.0;
+    double kf = -INFINITY, kf_other = -INFINITY; /* the follow id's block key, and the best key of other blocks */
+    int fq = fslot >= 0 ? block_of(ID_OF(fslot)) : -1;
+    for (int i0 = 0; i0 < n;) {
+        const int q = block_of(ID_OF(ord[i0]));
+        int i1 = i0;
+        double S = 0.0;
+        while (i1 < n && block_of(ID_OF(ord[i1])) == q) S += exp(l[ord[i1++]] / T - M);
+        total += S;
+        if (S > 0.0) {
+            const double key = log(S) + oracle_gumbel(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * q));
+            if (J < 0 || key > k1) {
+                k2 = k1;
+                k1 = key;
+                J = q;
+                Jbeg = i0;
+                Jend = i1;
+                SJ = S;
+            } else if (key > k2) {
+                k2 = key;
+            }
+            if (q == fq) kf = key;
+            else if (key > kf_other) kf_other = key;
+        }
+        i0 = i1;
+    }
+    /* inverse CDF inside the winner, ascending ids */
+    const double u = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * J + 1));
+    const double target = u * SJ;
+    int tok = -1;
+    double cum = 0.0, A = 0.0, m = 0.0;
+    for (int i = Jbeg; i < Jend && tok < 0; ++i) {
+        const double pv = exp(l[ord[i]] / T - M);
+        if (cum + pv > target && pv > 0.0) {
+            tok = ord[i];
+            A = cum;
+            m = pv;
+        }
+        cum += pv;
+    }
+    if (tok < 0) /* only if rounding put the target at the block's mass: the last member with mass */
+        for (int i = Jend - 1; i >= Jbeg && tok < 0; --i)
+            if (exp(l[ord[i]] / T - M) > 0.0) {
+                tok = ord[i];
+                m = exp(l[ord[i]] / T - M);
+                A = SJ - m;
+            }
+    const double C = SJ - A - m > 0.0 ? SJ - A - m : 0.0;
+    double margin = (k2 > -INFINITY) ? k1 - k2 : INFINITY;
+    if (A > 0.0) {
+        const double d = log(u * (m + C)) - log((1.0 - u) * A);
+        if (d < margin) margin = d;
+    }
+    if (C > 0.0) {
+        const double d = log((1.0 - u) * (A + m)) - log(u * C);
+        if (d < margin) margin = d;
+    }
+    out->slot = tok;
+    out->margin = margin;
+    out->lse = M + log(total);
+    out->logprob = l[tok] / T - out->lse;
+    if (fslot >= 0) {
+        out->lp_follow = l[fslot] / T - out->lse;
+        if (fslot == tok) {
+            out->reach = 1;
+        } else {
+            /* f's block against the others */
+            int race_ok = (kf > -INFINITY) && (kf_other == -INFINITY || kf >= kf_other - 2.0 * eps);
+            /* f inside its block */
+            double Af = 0.0, mf = 0.0, Cf = 0.0;
+            int seen = 0;
+            for (int i = 0; i < n; ++i) {
+                const int s = ord[i];
+                if (block_of(ID_OF(s)) != fq) continue;
+                const double pv = exp(l[s] / T - M);
+                if (s == fslot) {
+                    mf = pv;
+                    seen = 1;
+                } else if (!seen) {
+                    Af += pv;
+                } else {
+                    Cf += pv;
+                }
+            }
+            const double uf = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * fq + 1));
+            const double ep = exp(eps), em = exp(-eps), m1 = mf * ep;
+            const double zmin = (1.0 - uf) * Af * em - uf * Cf * ep;
+            const double zmax = (1.0 - uf) * Af * ep - uf * Cf * em;
+            const int in_ok = mf > 0.0 && zmin <= uf * m1 && zmax > -(1.0 - uf) * m1;
+            out->reach = race_ok && in_ok;
+        }
+    }
+    free(ord);
 }
 
-/* Draw over the whole vocabulary in sampling mode ([DSp] "DSpark vs DFlash 2": sample from the corrected
- * logits; the pages fix the distribution, softmax(l/T), not the sampler).  A two-level exponential race:
- * with p_v = exp(l_v/T - M), M = max l/T, the ids are grouped in aligned blocks of 16 (the last block may
- * be short); block j has mass S_j = sum of its p_v and one race variate E_j = -ln u(seed,row,pos, 2j).  The
- * block with the largest S_j / E_j wins (ties to the lower block); inside it the id is the first whose
- * inclusive prefix mass exceeds u(seed,row,pos, 2j+1) * S_j.  The minimum over blocks of E_j / S_j is
- * exponential with rate sum S and its arg-min is block j with probability S_j / sum S (independent
- * exponentials), and the inverse CDF then takes v with probability p_v / S_j: the draw is exactly
- * softmax(l/T).
- * Margin (how far the draw is from changing under small perturbations of l/T): the smaller of the top-2
- * log race-value gap and the target's distance to the nearest interior prefix boundary of the winning
- * block relative to its mass; a relative change eps of the masses moves both by about eps.
- * Returns the id; writes margin, the log-softmax of l/T at the id and the log-sum-exp. */
-static int draw_blocks(const double* l, int V, uint64_t seed, int row, int pos, double T, double* margin,
-                       double* logprob, double* lse_out) {
-    double M = -INFINITY;
-    for (int v = 0; v < V; ++v)
-        if (l[v] / T > M) M = l[v] / T;
-    const int nb = (V + 15) / 16;
-    double total = 0.0, k1 = -INFINITY, k2 = -INFINITY;
-    int J = -1;
-    for (int j = 0; j < nb; ++j) {
-        const int v1 = (16 * j + 16 < V) ? 16 * j + 16 : V;
-        double S = 0.0;
-        for (int v = 16 * j; v < v1; ++v) S += exp(l[v] / T - M);
-        total += S;
-        if (!(S > 0.0)) continue;
-        const double u1 = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * j));
-        const double key = log(S) - log(-log(u1));
-        if (J < 0 || key > k1) {
-            k2 = k1;
-            k1 = key;
-            J = j;
-        } else if (key > k2) {
-            k2 = key;
-        }
-    }
-    const int v0 = 16 * J, v1 = (v0 + 16 < V) ? v0 + 16 : V;
-    double SJ = 0.0;
-    for (int v = v0; v < v1; ++v) SJ += exp(l[v] / T - M);
-    const double target = oracle_noise_uniform(seed, (uint32_t)row, (uint32_t)pos, (uint32_t)(2 * J + 1)) * SJ;
-    int tok = -1;
-    double cum = 0.0, dist = INFINITY;
-    for (int v = v0; v < v1; ++v) {
-        const double pv = exp(l[v] / T - M);
-        cum += pv;
-        if (tok < 0 && cum > target) tok = v;
-        if (v + 1 < v1) {  /* interior boundary after id v */
-            const double d = fabs(target - cum) / SJ;
-            if (d < dist) dist = d;
-        }
-    }
-    if (tok < 0) /* the target sits at the block's mass: the last id with mass */
-        for (int v = v1 - 1; v >= v0 && tok < 0; --v)
-            if (exp(l[v] / T - M) > 0.0) tok = v;
-    const double lse = M + log(total);
-    if (margin) *margin = (k1 - k2 < dist) ? k1 - k2 : dist;
-    if (logprob) *logprob = l[tok] / T - lse;
-    if (lse_out) *lse_out = lse;
-    return tok;
-}
+#undef ID_OF
 
 /* ------------------------------------------------------------------------------------------ */
 /* O-M: full-vocabulary Markov head, K serial positions                                         */
@@ -376,14 +494,14 @@ static int draw_blocks(const double* l, int V, uint64_t seed, int row, int pos, 
  * H: [B, K, r] gate values or NULL.  follow: [B, K] or NULL -- when given, the predecessor of position
  * k > 0 is follow[b, k-1] instead of the oracle's own pick (teacher forcing along a given path).
  * rows: list of nrows row ids to compute (NULL: all B rows).
- * Outputs at [b*K + k]: tokens, logprobs (log softmax at the pick), margins (greedy: top-2 logit gap;
- * sampling: the race margin of draw_blocks),
- * lp_follow (log softmax at follow[b,k], or NULL), best_logit (l at the pick, or NULL). */
+ * Outputs at [b*K + k]: tokens, logprobs (log softmax at the pick), margins (see choose()), lp_follow (log
+ * softmax at follow[b,k], or NULL), best_logit (l at the pick, or NULL), reach (follow[b,k] is the pick or
+ * reachable by a perturbation of at most eps, see choose(); or NULL). */
 void oracle_markov_draft(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
                          const int32_t* anchor, const double* H, int B, int K, int V, int r, int mode,
                          uint64_t seed, double temperature, const int32_t* follow, const int32_t* rows,
                          int nrows, int32_t* tokens, double* logprobs, double* margins, double* lp_follow,
-                         double* best_logit) {
+                         double* best_logit, int32_t* reach, double eps) {
     int n = rows ? nrows : B;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int ri = 0; ri < n; ++ri) {
@@ -396,20 +514,19 @@ void oracle_markov_draft(const float* U, const void* W1, const void* W2, int wdt
             const double* Hk = H ? H + ((size_t)b * K + k) * (size_t)r : NULL;
             predecessor_embedding(W1, wdtype, r, prev, Hk, x);
             for (int v = 0; v < V; ++v) l[v] = calibrated_logit(Uk, W2, wdtype, w2_layout, V, r, x, v);
-            double margin, lp, lse;
-            int tok = (mode == OR_SAMPLE) ? draw_blocks(l, V, seed, b, k, temperature, &margin, &lp, &lse)
-                                          : pick(l, NULL, V, mode, seed, b, k, temperature, &margin, &lp, &lse);
             size_t o = (size_t)b * K + k;
-            tokens[o] = tok;
-            if (logprobs) logprobs[o] = lp;
-            if (margins) margins[o] = margin;
-            if (best_logit) best_logit[o] = l[tok];
-            double Teff = (mode == OR_SAMPLE) ? temperature : 1.0;
+            pick_out p;
+            choose(l, NULL, V, mode, seed, b, k, temperature, follow ? follow[o] : -1, eps, &p);
+            tokens[o] = p.slot;
+            if (logprobs) logprobs[o] = p.logprob;
+            if (margins) margins[o] = p.margin;
+            if (best_logit) best_logit[o] = l[p.slot];
             if (follow) {
-                if (lp_follow) lp_follow[o] = l[follow[o]] / Teff - lse;
-                prev = follow[o];
+                if (lp_follow) lp_follow[o] = p.lp_follow;
+                if (reach) reach[o] = p.reach;
+                prev = (follow[o] >= 0 && follow[o] < V) ? follow[o] : p.slot;
             } else {
-                prev = tok;
+                prev = p.slot;
             }
         }
         free(l);
@@ -489,12 +606,13 @@ void oracle_topk(const float* U, int64_t u_stride, int rows, int V, int k, int32
 
 /* The plain definition of what the truncated execution computes: O-M with the vocabulary at position
  * k replaced by the candidate set cand[b, k, 0..topk).  Pick, margin and log-softmax range over that
- * set.  Same argument meaning as oracle_markov_draft; cand is [B, K, topk]. */
+ * set (choose(), ascending ids).  Same argument meaning as oracle_markov_draft; cand is [B, K, topk].  A
+ * follow id that is not a candidate gets lp_follow = NaN and reach = 0 (its predecessor role still holds). */
 void oracle_markov_restricted(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
                               const int32_t* anchor, const double* H, const int32_t* cand, int B, int K,
                               int V, int r, int topk, int mode, uint64_t seed, double temperature,
-                              const int32_t* rows, int nrows, int32_t* tokens, double* logprobs,
-                              double* margins) {
+                              const int32_t* follow, const int32_t* rows, int nrows, int32_t* tokens,
+                              double* logprobs, double* margins, double* lp_follow, int32_t* reach, double eps) {
     int n = rows ? nrows : B;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int ri = 0; ri < n; ++ri) {
@@ -508,13 +626,19 @@ void oracle_markov_restricted(const float* U, const void* W1, const void* W2, in
             const int32_t* c = cand + ((size_t)b * K + k) * (size_t)topk;
             predecessor_embedding(W1, wdtype, r, prev, Hk, x);
             for (int s = 0; s < topk; ++s) l[s] = calibrated_logit(Uk, W2, wdtype, w2_layout, V, r, x, c[s]);
-            double margin, lp;
-            int slot = pick(l, c, topk, mode, seed, b, k, temperature, &margin, &lp, NULL);
             size_t o = (size_t)b * K + k;
-            tokens[o] = c[slot];
-            if (logprobs) logprobs[o] = lp;
-            if (margins) margins[o] = margin;
-            prev = c[slot];
+            pick_out p;
+            choose(l, c, topk, mode, seed, b, k, temperature, follow ? follow[o] : -1, eps, &p);
+            tokens[o] = c[p.slot];
+            if (logprobs) logprobs[o] = p.logprob;
+            if (margins) margins[o] = p.margin;
+            if (follow) {
+                if (lp_follow) lp_follow[o] = p.lp_follow;
+                if (reach) reach[o] = p.reach;
+                prev = (follow[o] >= 0 && follow[o] < V) ? follow[o] : c[p.slot];
+            } else {
+                prev = c[p.slot];
+            }
         }
         free(l);
         free(x);
@@ -532,8 +656,8 @@ void oracle_markov_restricted(const float* U, const void* W1, const void* W2, in
  *     and for t = 1..K-1 the k x k table of predecessor i, candidate j
  *       T_t[i][j]  = U_t(c_tj) + < A[c_{t-1,i}] (.) H_t, Bemb[c_tj] >
  *     ([MvS] "What the two methods do": S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>);
- *  3. walk: pick over the anchor row, then over row i_{t-1} of each table (greedy, or Gumbel-max with
- *     the noise keyed on the vocabulary id of the candidate).
+ *  3. walk: pick over the anchor row, then over row i_{t-1} of each table (choose(): greedy, or the
+ *     block race over the candidates, its noise keyed on vocabulary blocks, never on candidate slots).
  * A, Bemb: [V, r].  H: [B, K, r] or NULL.  cand_out: [B, K, topk] or NULL.
  * tables_out: [B, topk + (K-1)*topk*topk] (anchor row, then the tables) or NULL.
  * logprobs: log softmax of the walked row's scores/T at the pick. */
@@ -579,12 +703,13 @@ void oracle_selector_draft(const float* U, const void* A, const void* Bemb, int 
         for (int t = 0; t < K; ++t) {
             const double* src = (t == 0) ? tab : tab + topk + ((size_t)(t - 1) * topk + islot) * topk;
             for (int j = 0; j < topk; ++j) row[j] = src[j];
-            double margin, lp;
-            islot = pick(row, cand + (size_t)t * topk, topk, mode, seed, b, t, temperature, &margin, &lp, NULL);
+            pick_out p;
+            choose(row, cand + (size_t)t * topk, topk, mode, seed, b, t, temperature, -1, 0.0, &p);
+            islot = p.slot;
             size_t o = (size_t)b * K + t;
             tokens[o] = cand[(size_t)t * topk + islot];
-            if (logprobs) logprobs[o] = lp;
-            if (margins) margins[o] = margin;
+            if (logprobs) logprobs[o] = p.logprob;
+            if (margins) margins[o] = p.margin;
         }
         if (cand_out) memcpy(cand_out + (size_t)b * K * topk, cand, sizeof(int32_t) * (size_t)K * topk);
         if (tables_out) memcpy(tables_out + (size_t)b * tstride, tab, sizeof(double) * tstride);

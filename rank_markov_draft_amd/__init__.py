@@ -9,6 +9,7 @@ The library is loaded at import; if it is missing or cannot be loaded, the impor
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -44,6 +45,10 @@ def _load_lib():
         "dspark_markov_draft": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz, vp], i32),
         "dspark_markov_draft_timed": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, sz,
                                        vp, vp, vp, vp], i32),
+        "dspark_markov_draft_logits": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp,
+                                        sz, vp], i32),
+        "dspark_markov_status": ([vp, sz, i32, i32, vp], i32),
+        "dspark_set_spin_limit": ([ctypes.c_uint32], None),
         "dspark_markov_draft_confidence": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, i32, vp,
                                             vp, vp, vp, vp, vp, sz, vp], i32),
         "dspark_markov_step": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp, sz,
@@ -107,6 +112,12 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocations of a call that enqueues on ``stream`` are made with that stream current, so the caching
+    allocator orders their reuse after the call's kernels (a temporary workspace is freed on return)."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def dspark_abi_version() -> int:
     return int(_lib.dspark_abi_version())
 
@@ -125,173 +136,219 @@ def dspark_markov_draft(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mo
                         temperature=1.0, tokens=None, logprobs=None, want_logprobs=True, workspace=None, stream=None):
     """K-position Markov-head draft.  U [B,K,V] fp32; W1 [V,r]; W2 [V,r] (DSPARK_W2_VR) or [r,V] (DSPARK_W2_RV);
     anchor [B] int32; H [B,K,r] fp32 or None.  Returns (tokens [B,K] int32, logprobs [B,K] fp32 or None)."""
-    _dev(U, "U", torch.float32, 3)
-    B, K, V = U.shape
-    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
-    _dev(W2, "W2", W1.dtype, 2)
-    r = W1.shape[1]
-    _dev(anchor, "anchor", torch.int32, 1)
-    if H is not None:
-        _dev(H, "H", torch.float32, 3)
-    wd = _wdtype(W1)
-    if tokens is None:
+    with _on(stream):
+        _dev(U, "U", torch.float32, 3)
+        B, K, V = U.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(anchor, "anchor", torch.int32, 1)
+        if H is not None:
+            _dev(H, "H", torch.float32, 3)
+        wd = _wdtype(W1)
+        if tokens is None:
+            tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
+        if logprobs is None and want_logprobs:
+            logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device)
+        ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+        _check(_lib.dspark_markov_draft(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r, mode, seed,
+                                        float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb, _stream(stream)),
+               "dspark_markov_draft")
+        return tokens, logprobs
+
+
+def dspark_markov_draft_logits(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY, seed=0,
+                               temperature=1.0, workspace=None, stream=None):
+    """Validation: dspark_markov_draft that also returns the calibrated logits [B, K, V] fp32 of every position
+    along the drafted path, written by the whole-round kernel.  Returns (tokens, logprobs, logits)."""
+    with _on(stream):
+        _dev(U, "U", torch.float32, 3)
+        B, K, V = U.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(anchor, "anchor", torch.int32, 1)
+        if H is not None:
+            _dev(H, "H", torch.float32, 3)
+        wd = _wdtype(W1)
         tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
-    if logprobs is None and want_logprobs:
         logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device)
-    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
-    _check(_lib.dspark_markov_draft(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r, mode, seed,
-                                    float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb, _stream(stream)),
-           "dspark_markov_draft")
-    return tokens, logprobs
+        logits = torch.empty((B, K, V), dtype=torch.float32, device=U.device)
+        ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+        _check(_lib.dspark_markov_draft_logits(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r,
+                                               mode, seed, float(temperature), _p(tokens), _p(logprobs), _p(logits),
+                                               _p(ws), wsb, _stream(stream)), "dspark_markov_draft_logits")
+        return tokens, logprobs, logits
+
+
+def dspark_markov_status(workspace, B, K, *, stream=None):
+    """Device-side status of the last draft made with ``workspace`` (a uint8 device tensor): DSPARK_OK, or
+    DSPARK_EDEVICE if a bounded wait of the whole-round kernel gave up.  Synchronises with the stream."""
+    with _on(stream):
+        return int(_lib.dspark_markov_status(_p(workspace), workspace.numel() * workspace.element_size(), B, K,
+                                             _stream(stream)))
+
+
+def dspark_set_spin_limit(sleeps: int):
+    """Testing hook: bound of the round kernel's waits for later calls (0 restores the default)."""
+    _lib.dspark_set_spin_limit(int(sleeps))
 
 
 def dspark_markov_draft_confidence(U, W1, W2, anchor, h, conf_w, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY,
                                    seed=0, temperature=1.0, want_logprobs=True, workspace=None, stream=None):
     """Draft plus the confidence head: h [B,K,D] bf16, conf_w [D+r] fp32 (h part, then W1 part).  Returns
     (tokens, logprobs or None, conf [B,K] fp32, survival [B,K] fp32)."""
-    _dev(U, "U", torch.float32, 3)
-    B, K, V = U.shape
-    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
-    _dev(W2, "W2", W1.dtype, 2)
-    r = W1.shape[1]
-    _dev(anchor, "anchor", torch.int32, 1)
-    _dev(h, "h", torch.bfloat16, 3)
-    _dev(conf_w, "conf_w", torch.float32, 1)
-    if H is not None:
-        _dev(H, "H", torch.float32, 3)
-    D = h.shape[2]
-    if tuple(h.shape[:2]) != (B, K) or conf_w.shape[0] != D + r:
-        raise ValueError("h must be [B, K, D] and conf_w [D + r]")
-    wd = _wdtype(W1)
-    tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
-    logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device) if want_logprobs else None
-    conf = torch.empty((B, K), dtype=torch.float32, device=U.device)
-    surv = torch.empty((B, K), dtype=torch.float32, device=U.device)
-    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
-    _check(_lib.dspark_markov_draft_confidence(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r,
-                                               mode, seed, float(temperature), _p(h), D, _p(conf_w), _p(tokens),
-                                               _p(logprobs), _p(conf), _p(surv), _p(ws), wsb, _stream(stream)),
-           "dspark_markov_draft_confidence")
-    return tokens, logprobs, conf, surv
+    with _on(stream):
+        _dev(U, "U", torch.float32, 3)
+        B, K, V = U.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(anchor, "anchor", torch.int32, 1)
+        _dev(h, "h", torch.bfloat16, 3)
+        _dev(conf_w, "conf_w", torch.float32, 1)
+        if H is not None:
+            _dev(H, "H", torch.float32, 3)
+        D = h.shape[2]
+        if tuple(h.shape[:2]) != (B, K) or conf_w.shape[0] != D + r:
+            raise ValueError("h must be [B, K, D] and conf_w [D + r]")
+        wd = _wdtype(W1)
+        tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
+        logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device) if want_logprobs else None
+        conf = torch.empty((B, K), dtype=torch.float32, device=U.device)
+        surv = torch.empty((B, K), dtype=torch.float32, device=U.device)
+        ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+        _check(_lib.dspark_markov_draft_confidence(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r,
+                                                   mode, seed, float(temperature), _p(h), D, _p(conf_w), _p(tokens),
+                                                   _p(logprobs), _p(conf), _p(surv), _p(ws), wsb, _stream(stream)),
+               "dspark_markov_draft_confidence")
+        return tokens, logprobs, conf, surv
 
 
 def dspark_markov_draft_timed(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=None, mode=DSPARK_GREEDY, seed=0,
                               temperature=1.0, tokens=None, logprobs=None, workspace=None, stream=None):
     """dspark_markov_draft plus contraction-kernel timing (HIP events on the same stream).
     Returns (tokens, logprobs, kernel_ms summed over the contraction launches, number of launches, round_ms)."""
-    _dev(U, "U", torch.float32, 3)
-    B, K, V = U.shape
-    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
-    _dev(W2, "W2", W1.dtype, 2)
-    r = W1.shape[1]
-    _dev(anchor, "anchor", torch.int32, 1)
-    if H is not None:
-        _dev(H, "H", torch.float32, 3)
-    wd = _wdtype(W1)
-    if tokens is None:
-        tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
-    if logprobs is None:
-        logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device)
-    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
-    kernel_ms = ctypes.c_float()
-    launches = ctypes.c_int()
-    round_ms = ctypes.c_float()
-    _check(_lib.dspark_markov_draft_timed(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r, mode,
-                                          seed, float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb,
-                                          _stream(stream), ctypes.byref(kernel_ms), ctypes.byref(launches),
-                                          ctypes.byref(round_ms)), "dspark_markov_draft_timed")
-    return tokens, logprobs, float(kernel_ms.value), int(launches.value), float(round_ms.value)
+    with _on(stream):
+        _dev(U, "U", torch.float32, 3)
+        B, K, V = U.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(anchor, "anchor", torch.int32, 1)
+        if H is not None:
+            _dev(H, "H", torch.float32, 3)
+        wd = _wdtype(W1)
+        if tokens is None:
+            tokens = torch.empty((B, K), dtype=torch.int32, device=U.device)
+        if logprobs is None:
+            logprobs = torch.empty((B, K), dtype=torch.float32, device=U.device)
+        ws, wsb = _workspace(dspark_markov_workspace_bytes(B, K, V, r, wd, w2_layout), U.device, workspace)
+        kernel_ms = ctypes.c_float()
+        launches = ctypes.c_int()
+        round_ms = ctypes.c_float()
+        _check(_lib.dspark_markov_draft_timed(_p(U), _p(W1), _p(W2), wd, w2_layout, _p(anchor), _p(H), B, K, V, r, mode,
+                                              seed, float(temperature), _p(tokens), _p(logprobs), _p(ws), wsb,
+                                              _stream(stream), ctypes.byref(kernel_ms), ctypes.byref(launches),
+                                              ctypes.byref(round_ms)), "dspark_markov_draft_timed")
+        return tokens, logprobs, float(kernel_ms.value), int(launches.value), float(round_ms.value)
 
 
 def dspark_markov_step(U_k, W1, W2, prev, k, *, w2_layout=DSPARK_W2_VR, H_k=None, mode=DSPARK_GREEDY, seed=0,
                        temperature=1.0, workspace=None, stream=None):
     """One position with supplied predecessors.  U_k [B,V] fp32 (rows may be strided); prev [B] int32.
     Returns (tok [B], logprob [B], best_logit [B])."""
-    if not U_k.is_cuda or U_k.dtype != torch.float32 or U_k.dim() != 2 or U_k.stride(1) != 1:
-        raise ValueError("U_k must be a GPU float32 [B, V] tensor with unit column stride")
-    B, V = U_k.shape
-    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
-    _dev(W2, "W2", W1.dtype, 2)
-    r = W1.shape[1]
-    _dev(prev, "prev", torch.int32, 1)
-    if H_k is not None:
-        _dev(H_k, "H_k", torch.float32, 2)
-    wd = _wdtype(W1)
-    tok = torch.empty(B, dtype=torch.int32, device=U_k.device)
-    lp = torch.empty(B, dtype=torch.float32, device=U_k.device)
-    bl = torch.empty(B, dtype=torch.float32, device=U_k.device)
-    ws, wsb = _workspace(dspark_markov_workspace_bytes(B, 1, V, r, wd, w2_layout), U_k.device, workspace)
-    _check(_lib.dspark_markov_step(_p(U_k), U_k.stride(0), _p(W1), _p(W2), wd, w2_layout, _p(prev), _p(H_k), B, V, r,
-                                   int(k), mode, seed, float(temperature), _p(tok), _p(lp), _p(bl), _p(ws), wsb,
-                                   _stream(stream)), "dspark_markov_step")
-    return tok, lp, bl
+    with _on(stream):
+        if not U_k.is_cuda or U_k.dtype != torch.float32 or U_k.dim() != 2 or U_k.stride(1) != 1:
+            raise ValueError("U_k must be a GPU float32 [B, V] tensor with unit column stride")
+        B, V = U_k.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(prev, "prev", torch.int32, 1)
+        if H_k is not None:
+            _dev(H_k, "H_k", torch.float32, 2)
+        wd = _wdtype(W1)
+        tok = torch.empty(B, dtype=torch.int32, device=U_k.device)
+        lp = torch.empty(B, dtype=torch.float32, device=U_k.device)
+        bl = torch.empty(B, dtype=torch.float32, device=U_k.device)
+        ws, wsb = _workspace(dspark_markov_workspace_bytes(B, 1, V, r, wd, w2_layout), U_k.device, workspace)
+        _check(_lib.dspark_markov_step(_p(U_k), U_k.stride(0), _p(W1), _p(W2), wd, w2_layout, _p(prev), _p(H_k), B, V, r,
+                                       int(k), mode, seed, float(temperature), _p(tok), _p(lp), _p(bl), _p(ws), wsb,
+                                       _stream(stream)), "dspark_markov_step")
+        return tok, lp, bl
 
 
 def dspark_markov_logits(U_k, W1, W2, prev, *, w2_layout=DSPARK_W2_VR, H_k=None, out=None, stream=None):
     """Calibrated logits of one position, [B, V] fp32 (validation path)."""
-    if not U_k.is_cuda or U_k.dtype != torch.float32 or U_k.dim() != 2 or U_k.stride(1) != 1:
-        raise ValueError("U_k must be a GPU float32 [B, V] tensor with unit column stride")
-    B, V = U_k.shape
-    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
-    _dev(W2, "W2", W1.dtype, 2)
-    r = W1.shape[1]
-    _dev(prev, "prev", torch.int32, 1)
-    if H_k is not None:
-        _dev(H_k, "H_k", torch.float32, 2)
-    wd = _wdtype(W1)
-    if out is None:
-        out = torch.empty((B, V), dtype=torch.float32, device=U_k.device)
-    need = V * r * W1.element_size() if w2_layout == DSPARK_W2_RV else 0
-    ws, wsb = _workspace(need, U_k.device, None)
-    _check(_lib.dspark_markov_logits(_p(U_k), U_k.stride(0), _p(W1), _p(W2), wd, w2_layout, _p(prev), _p(H_k), B, V, r,
-                                     _p(out), _p(ws), wsb, _stream(stream)), "dspark_markov_logits")
-    return out
+    with _on(stream):
+        if not U_k.is_cuda or U_k.dtype != torch.float32 or U_k.dim() != 2 or U_k.stride(1) != 1:
+            raise ValueError("U_k must be a GPU float32 [B, V] tensor with unit column stride")
+        B, V = U_k.shape
+        _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+        _dev(W2, "W2", W1.dtype, 2)
+        r = W1.shape[1]
+        _dev(prev, "prev", torch.int32, 1)
+        if H_k is not None:
+            _dev(H_k, "H_k", torch.float32, 2)
+        wd = _wdtype(W1)
+        if out is None:
+            out = torch.empty((B, V), dtype=torch.float32, device=U_k.device)
+        need = V * r * W1.element_size() if w2_layout == DSPARK_W2_RV else 0
+        ws, wsb = _workspace(need, U_k.device, None)
+        _check(_lib.dspark_markov_logits(_p(U_k), U_k.stride(0), _p(W1), _p(W2), wd, w2_layout, _p(prev), _p(H_k), B, V, r,
+                                         _p(out), _p(ws), wsb, _stream(stream)), "dspark_markov_logits")
+        return out
 
 
 def dspark_pack_w2(W2_rv, *, out=None, stream=None):
     """[r, V] -> [V, r] copy of W2."""
-    _dev(W2_rv, "W2", (torch.bfloat16, torch.float32), 2)
-    r, V = W2_rv.shape
-    if out is None:
-        out = torch.empty((V, r), dtype=W2_rv.dtype, device=W2_rv.device)
-    _check(_lib.dspark_pack_w2(_p(W2_rv), V, r, _wdtype(W2_rv), _p(out), _stream(stream)), "dspark_pack_w2")
-    return out
+    with _on(stream):
+        _dev(W2_rv, "W2", (torch.bfloat16, torch.float32), 2)
+        r, V = W2_rv.shape
+        if out is None:
+            out = torch.empty((V, r), dtype=W2_rv.dtype, device=W2_rv.device)
+        _check(_lib.dspark_pack_w2(_p(W2_rv), V, r, _wdtype(W2_rv), _p(out), _stream(stream)), "dspark_pack_w2")
+        return out
 
 
 def dspark_stream_read(a, b, sink, *, stream=None):
     """Reads the contiguous device tensors a and b once (measurement utility); sink: a 1-element int32 tensor."""
-    for t, n in ((a, "a"), (b, "b"), (sink, "sink")):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise ValueError(f"{n} must be a contiguous device tensor")
-    _check(_lib.dspark_stream_read(_p(a), a.numel() * a.element_size(), _p(b), b.numel() * b.element_size(), _p(sink),
-                                   _stream(stream)), "dspark_stream_read")
+    with _on(stream):
+        for t, n in ((a, "a"), (b, "b"), (sink, "sink")):
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError(f"{n} must be a contiguous device tensor")
+        _check(_lib.dspark_stream_read(_p(a), a.numel() * a.element_size(), _p(b), b.numel() * b.element_size(), _p(sink),
+                                       _stream(stream)), "dspark_stream_read")
 
 
 def dspark_gate(h, Wg, *, out=None, stream=None):
     """H = sigmoid(h Wg): h [..., D] bf16, Wg [D, r] bf16 -> [..., r] fp32."""
-    _dev(h, "h", torch.bfloat16)
-    _dev(Wg, "Wg", torch.bfloat16, 2)
-    D, r = Wg.shape
-    if h.shape[-1] != D:
-        raise ValueError("h's last dim must equal Wg's first")
-    rows = h.numel() // D
-    if out is None:
-        out = torch.empty(tuple(h.shape[:-1]) + (r,), dtype=torch.float32, device=h.device)
-    _check(_lib.dspark_gate(_p(h), _p(Wg), rows, D, r, _p(out), _stream(stream)), "dspark_gate")
-    return out
+    with _on(stream):
+        _dev(h, "h", torch.bfloat16)
+        _dev(Wg, "Wg", torch.bfloat16, 2)
+        D, r = Wg.shape
+        if h.shape[-1] != D:
+            raise ValueError("h's last dim must equal Wg's first")
+        rows = h.numel() // D
+        if out is None:
+            out = torch.empty(tuple(h.shape[:-1]) + (r,), dtype=torch.float32, device=h.device)
+        _check(_lib.dspark_gate(_p(h), _p(Wg), rows, D, r, _p(out), _stream(stream)), "dspark_gate")
+        return out
 
 
 def dspark_topk(U, topk, *, want_values=True, stream=None):
     """Top-k ids (value desc, id asc) of every row of U [..., V] fp32 -> (idx int32, val fp32 or None)."""
-    _dev(U, "U", torch.float32)
-    V = U.shape[-1]
-    rows = U.numel() // V
-    idx = torch.empty(tuple(U.shape[:-1]) + (topk,), dtype=torch.int32, device=U.device)
-    val = torch.empty(tuple(U.shape[:-1]) + (topk,), dtype=torch.float32, device=U.device) if want_values else None
-    nbytes = int(_lib.dspark_topk_workspace_bytes(rows, V, topk))
-    ws, wsb = _workspace(nbytes, U.device, None)
-    _check(_lib.dspark_topk(_p(U), V, rows, V, topk, _p(idx), _p(val), _p(ws), wsb, _stream(stream)), "dspark_topk")
-    return idx, val
+    with _on(stream):
+        _dev(U, "U", torch.float32)
+        V = U.shape[-1]
+        rows = U.numel() // V
+        idx = torch.empty(tuple(U.shape[:-1]) + (topk,), dtype=torch.int32, device=U.device)
+        val = torch.empty(tuple(U.shape[:-1]) + (topk,), dtype=torch.float32, device=U.device) if want_values else None
+        nbytes = int(_lib.dspark_topk_workspace_bytes(rows, V, topk))
+        ws, wsb = _workspace(nbytes, U.device, None)
+        _check(_lib.dspark_topk(_p(U), V, rows, V, topk, _p(idx), _p(val), _p(ws), wsb, _stream(stream)), "dspark_topk")
+        return idx, val
 
 
 def dspark_selector_workspace_bytes(B, K, V, r, topk) -> int:
@@ -301,39 +358,41 @@ def dspark_selector_workspace_bytes(B, K, V, r, topk) -> int:
 def dspark_schedule_prefixes(survival, sps, *, stream=None):
     """Greedy load-aware prefix scheduling.  survival [R, K] fp32, sps [R (K + 1) + 1] fp32 (steps per second by
     target batch size).  Returns (lengths [R] int32, theta [1] fp32)."""
-    _dev(survival, "survival", torch.float32, 2)
-    R, K = survival.shape
-    _dev(sps, "sps", torch.float32, 1)
-    if sps.shape[0] != R * (K + 1) + 1:
-        raise ValueError("sps must have R (K + 1) + 1 entries")
-    lengths = torch.empty((R,), dtype=torch.int32, device=survival.device)
-    theta = torch.empty((1,), dtype=torch.float32, device=survival.device)
-    _check(_lib.dspark_schedule_prefixes(_p(survival), _p(sps), R, K, _p(lengths), _p(theta), _stream(stream)),
-           "dspark_schedule_prefixes")
-    return lengths, theta
+    with _on(stream):
+        _dev(survival, "survival", torch.float32, 2)
+        R, K = survival.shape
+        _dev(sps, "sps", torch.float32, 1)
+        if sps.shape[0] != R * (K + 1) + 1:
+            raise ValueError("sps must have R (K + 1) + 1 entries")
+        lengths = torch.empty((R,), dtype=torch.int32, device=survival.device)
+        theta = torch.empty((1,), dtype=torch.float32, device=survival.device)
+        _check(_lib.dspark_schedule_prefixes(_p(survival), _p(sps), R, K, _p(lengths), _p(theta), _stream(stream)),
+               "dspark_schedule_prefixes")
+        return lengths, theta
 
 
 def dspark_selector_draft(U, A, Bemb, anchor, *, H=None, topk=16, mode=DSPARK_GREEDY, seed=0, temperature=1.0,
                           want_logprobs=True, want_cand=False, want_scores=False, workspace=None, stream=None):
     """Selector execution.  Returns dict(tokens, logprobs, cand, scores) (absent items are None)."""
-    _dev(U, "U", torch.float32, 3)
-    B, K, V = U.shape
-    _dev(A, "A", (torch.bfloat16, torch.float32), 2)
-    _dev(Bemb, "Bemb", A.dtype, 2)
-    r = A.shape[1]
-    _dev(anchor, "anchor", torch.int32, 1)
-    if H is not None:
-        _dev(H, "H", torch.float32, 3)
-    dev = U.device
-    tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
-    lp = torch.empty((B, K), dtype=torch.float32, device=dev) if want_logprobs else None
-    cand = torch.empty((B, K, topk), dtype=torch.int32, device=dev) if want_cand else None
-    scores = torch.empty((B, topk + (K - 1) * topk * topk), dtype=torch.float32, device=dev) if want_scores else None
-    ws, wsb = _workspace(dspark_selector_workspace_bytes(B, K, V, r, topk), dev, workspace)
-    _check(_lib.dspark_selector_draft(_p(U), _p(A), _p(Bemb), _wdtype(A), _p(anchor), _p(H), B, K, V, r, topk, mode,
-                                      seed, float(temperature), _p(tokens), _p(lp), _p(cand), _p(scores), _p(ws), wsb,
-                                      _stream(stream)), "dspark_selector_draft")
-    return dict(tokens=tokens, logprobs=lp, cand=cand, scores=scores)
+    with _on(stream):
+        _dev(U, "U", torch.float32, 3)
+        B, K, V = U.shape
+        _dev(A, "A", (torch.bfloat16, torch.float32), 2)
+        _dev(Bemb, "Bemb", A.dtype, 2)
+        r = A.shape[1]
+        _dev(anchor, "anchor", torch.int32, 1)
+        if H is not None:
+            _dev(H, "H", torch.float32, 3)
+        dev = U.device
+        tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+        lp = torch.empty((B, K), dtype=torch.float32, device=dev) if want_logprobs else None
+        cand = torch.empty((B, K, topk), dtype=torch.int32, device=dev) if want_cand else None
+        scores = torch.empty((B, topk + (K - 1) * topk * topk), dtype=torch.float32, device=dev) if want_scores else None
+        ws, wsb = _workspace(dspark_selector_workspace_bytes(B, K, V, r, topk), dev, workspace)
+        _check(_lib.dspark_selector_draft(_p(U), _p(A), _p(Bemb), _wdtype(A), _p(anchor), _p(H), B, K, V, r, topk, mode,
+                                          seed, float(temperature), _p(tokens), _p(lp), _p(cand), _p(scores), _p(ws), wsb,
+                                          _stream(stream)), "dspark_selector_draft")
+        return dict(tokens=tokens, logprobs=lp, cand=cand, scores=scores)
 
 
 def library():

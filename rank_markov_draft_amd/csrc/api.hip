@@ -27,6 +27,8 @@ int device_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxG = 1024;          // upper bound on workgroups along the vocabulary
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // sleeps before a bounded wait of the round kernel gives up
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
 constexpr int kRowPad = 128;         // partials are padded to whole 128-row blocks
 constexpr int kMfmaWGPerCU = 2;
 
@@ -229,7 +231,8 @@ bool coop_supported() {
 int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout, const int32_t* anchor,
                       const float* H, int B, int K, int V, int r, int mode, uint64_t seed, float temperature,
                       int32_t* tokens, float* logprobs, void* workspace, size_t workspace_bytes, void* stream,
-                      hipEvent_t* ev, int* kernel_launches, const ConfArgs* cf = nullptr) {
+                      hipEvent_t* ev, int* kernel_launches, const ConfArgs* cf = nullptr,
+                      float* logits_out = nullptr) {
     g_err[0] = 0;
     int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
     if (rc) return rc;
@@ -258,7 +261,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
                           aligned16(U) && V % 4 == 0 && (!H || aligned16(H)) && coop_supported();
     if (round_ok) {
         const int ntiles = (V + 31) / 32;
-        int G = round_max_coresident(r, sample, H != nullptr, round_small_block(B));
+        int G = round_max_coresident(r, sample, H != nullptr, round_small_block(B), logits_out != nullptr);
         if (G > round_gmax()) G = round_gmax();
         if (G > ntiles) G = ntiles;
         if (G >= 1) {
@@ -291,16 +294,23 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.logprobs = logprobs;
             a.inv_t = 1.0f / teff;
             if (cf) a.cf = *cf;
-            a.spin_limit = 1u << 22;
+            a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
             a.p_mc = ws.p_mc;
             a.p_s = ws.p_s;
             a.p_idx = ws.p_idx;
             a.p_l = ws.p_l;
+            a.logits_out = logits_out;
             hipError_t e = launch_markov_round(a, sample, H != nullptr, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
             if (e != hipSuccess) return device_fail(e, "draft round launch");
             if (kernel_launches) *kernel_launches = 1;
             return DSPARK_OK;
         }
+    }
+    if (logits_out) return fail(DSPARK_EUNSUPPORTED, "this shape does not take the whole-round kernel");
+    {
+        // this path has no bounded waits: clear the error word so dspark_markov_status reports this call
+        hipError_t e = launch_fill_u32(ws.counters + kErrorWord, 0u, 1, st);
+        if (e != hipSuccess) return device_fail(e, "error word clear");
     }
     // one launch pair (contraction, reduction) per position
     for (int k = 0; k < K; ++k) {
@@ -373,6 +383,34 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         void* stream) {
     return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
                              logprobs, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dspark_markov_status(const void* workspace, size_t workspace_bytes, int B, int K, void* stream) {
+    g_err[0] = 0;
+    if (!workspace) return fail(DSPARK_EINVAL, "workspace must not be NULL");
+    if (B <= 0 || K <= 0) return fail(DSPARK_EINVAL, "B and K must be positive");
+    const MarkovWs ws = carve_markov(const_cast<void*>(workspace), B, K);
+    const size_t end = (size_t)((const uint8_t*)(ws.counters + kErrorWord + 1) - (const uint8_t*)workspace);
+    if (workspace_bytes < end) return fail(DSPARK_EWORKSPACE, "workspace of %zu bytes too small for B=%d K=%d", workspace_bytes, B, K);
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "hipStreamSynchronize");
+    uint32_t err = 0;
+    e = hipMemcpy(&err, ws.counters + kErrorWord, sizeof err, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail(e, "reading the error word");
+    if (err) return fail(DSPARK_EDEVICE, "a bounded wait of the whole-round kernel gave up: tokens -1 / NaN where it failed");
+    return DSPARK_OK;
+}
+
+void dspark_set_spin_limit(uint32_t sleeps) { g_spin_limit.store(sleeps ? sleeps : kDefaultSpinLimit, std::memory_order_relaxed); }
+
+int dspark_markov_draft_logits(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                               const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                               uint64_t seed, float temperature, int32_t* tokens, float* logprobs, float* logits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!logits) return fail(DSPARK_EINVAL, "logits must not be NULL");
+    return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
+                             logprobs, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, logits);
 }
 
 int dspark_markov_draft_confidence(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
@@ -555,6 +593,7 @@ int dspark_selector_draft(const float* U, const void* A, const void* Bemb, int w
     if (mode == DSPARK_SAMPLE && !(temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0 when sampling");
     if (topk < 1 || topk > V) return fail(DSPARK_EINVAL, "topk %d outside [1, V]", topk);
     if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 64 needs V <= 4096");
+    if (topk > 1024) return fail(DSPARK_EUNSUPPORTED, "the walk takes at most 1024 candidates (topk = %d)", topk);
     if (r > 1024) return fail(DSPARK_EUNSUPPORTED, "r = %d exceeds 1024", r);
     if ((size_t)B * K > 2147483647u) return fail(DSPARK_EUNSUPPORTED, "B * K too large");
     const size_t need = dspark_selector_workspace_bytes(B, K, V, r, topk);

@@ -104,6 +104,7 @@ struct RoundArgs {
     float* p_s;
     int* p_idx;                 // [K][G][Bpad] best id and its logit per workgroup
     float* p_l;
+    float* logits_out;          // validation: [B, K, V] calibrated logits along the drafted path, or null
 };
 // Each (position, row) pick has kWinnerSlots words (workgroup g updates slot g % kWinnerSlots), each on a
 // 128-byte line of its own: every workgroup updates every row once per position, and atomics on one line are
@@ -120,7 +121,7 @@ constexpr int kCounterStride = 32;  // words between counters (128 bytes)
 int round_supported_r(int r);
 // A batch of at most 8 rows takes the round kernel's small-block form (one U unit per item, deeper stream).
 inline bool round_small_block(int B) { return B <= 8; }
-int round_max_coresident(int r, bool sample, bool gated, bool small);
+int round_max_coresident(int r, bool sample, bool gated, bool small, bool store = false);
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
                                hipEvent_t ev_end);
 
@@ -130,6 +131,7 @@ hipError_t launch_markov_step_valu(const StepArgsValu& a, bool bf16, int mode, b
 hipError_t launch_markov_reduce(const ReduceArgs& a, int B, hipStream_t st);
 
 hipError_t launch_transpose(const void* src, int rows, int cols, int elem_bytes, void* dst, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st);
 hipError_t launch_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, hipStream_t st);
 
 // gate: H = sigmoid(h Wg)

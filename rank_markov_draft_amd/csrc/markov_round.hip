@@ -227,7 +227,9 @@ __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) 
     }
 }
 
-template <int RK, int MODE, bool GATED, int UR>
+// STORE (validation only) also writes every tile's calibrated logits to a.logits_out [B, K, V] before its
+// epilogue; the contraction and the pick are the same code.
+template <int RK, int MODE, bool GATED, int UR, bool STORE = false>
 __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArgs a) {
     using RG = Ring<RK, UR>;
     constexpr bool SAMPLE = MODE == kModeSample;
@@ -486,6 +488,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     float bs = 0.f, bE = 1.f, be = 0.f;
     float bl = -INFINITY;        // greedy: best logit
     int bslot = 0, btile = -1;   // best id = 32 btile + 16 half + bslot
+    float* store_row = nullptr;  // STORE: this lane's row of the current position in a.logits_out, or null
     const float c = a.c;
     const int rho = lane & 31;
     const int cset = SETS > 1 ? wave / kRowWaves : 0;                    // tile slots cset, cset + SETS, ...
@@ -522,6 +525,23 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         const f32x8_t lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
         const f32x8_t hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    };
+    // STORE: the lane's 16 logits of tile t (ids 32 t + 16 half + j), ids past the vocabulary left out
+    auto store_tile = [&](const f32x16_t& lv, int t) {
+        if constexpr (STORE) {
+            if (!store_row) return;
+            const int v0 = t * kRTileV + 16 * half;
+            float* d = store_row + v0;
+            if (v0 + 16 <= a.V) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4_t*>(d + 4 * q) = f32x4_t{lv[4 * q], lv[4 * q + 1], lv[4 * q + 2], lv[4 * q + 3]};
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (v0 + j < a.V) d[j] = lv[j];
+            }
+        }
     };
     auto frag = [&](int i, int j) -> bf16x8_t {
         return *reinterpret_cast<const bf16x8_t*>(ring + (i % RG::kNS) * RG::kStage + a_off + 32 * j);
@@ -609,6 +629,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         fr[0] = frag(in, 0);
         if (RK > 1) fr[1] = frag(in, 1);
         __builtin_amdgcn_sched_barrier(0);
+        store_tile(cur, t);
         float mc;
         const float cm = tile_head(cur, t, kUnmasked, mc);
         float sb = 0.f, E = 1.f, target = 0.f, cum = 0.f, esel = 0.f;
@@ -640,6 +661,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         if (!SAMPLE) greedy_pick(cur, cm, t);
     };
     auto last = [&](f32x16_t& cur, int t, auto mask_tail) {
+        store_tile(cur, t);
         float mc;
         const float cm = tile_head(cur, t, mask_tail, mc);
         if (SAMPLE) {
@@ -749,6 +771,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             }
             if (SAMPLE) k2 = noise_key2(a.k0, (uint32_t)b, (uint32_t)k);
         }
+        if constexpr (STORE) store_row = valid_b ? a.logits_out + ((size_t)b * a.K + k) * (size_t)a.V : nullptr;
         m = kNegBig;
         s = 0.f;
         bs = 0.f;
@@ -964,34 +987,35 @@ int round_supported_r(int r) { return mfma_supported_r(r) && r <= 256; }
 
 
 template <int RK, int MODE, bool GATED, int UR>
-static const void* round_fn() {
-    return reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED, UR>);
+static const void* round_fn(bool store) {
+    return store ? reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED, UR, true>)
+                 : reinterpret_cast<const void*>(&markov_round_kernel<RK, MODE, GATED, UR, false>);
 }
 
 template <int RK, int MODE, bool GATED>
-static const void* round_fn(bool small) {
-    return small ? round_fn<RK, MODE, GATED, 1>() : round_fn<RK, MODE, GATED, 16>();
+static const void* round_fn(bool small, bool store) {
+    return small ? round_fn<RK, MODE, GATED, 1>(store) : round_fn<RK, MODE, GATED, 16>(store);
 }
 
 template <int RK>
-static const void* round_fn(bool sample, bool gated, bool small) {
-    if (sample) return gated ? round_fn<RK, kModeSample, true>(small) : round_fn<RK, kModeSample, false>(small);
-    return gated ? round_fn<RK, kModeGreedy, true>(small) : round_fn<RK, kModeGreedy, false>(small);
+static const void* round_fn(bool sample, bool gated, bool small, bool store) {
+    if (sample) return gated ? round_fn<RK, kModeSample, true>(small, store) : round_fn<RK, kModeSample, false>(small, store);
+    return gated ? round_fn<RK, kModeGreedy, true>(small, store) : round_fn<RK, kModeGreedy, false>(small, store);
 }
 
-static const void* round_fn_r(int r, bool sample, bool gated, bool small) {
+static const void* round_fn_r(int r, bool sample, bool gated, bool small, bool store) {
     switch (r / 16) {
-        case 1: return round_fn<1>(sample, gated, small);
-        case 2: return round_fn<2>(sample, gated, small);
-        case 4: return round_fn<4>(sample, gated, small);
-        case 8: return round_fn<8>(sample, gated, small);
-        case 16: return round_fn<16>(sample, gated, small);
+        case 1: return round_fn<1>(sample, gated, small, store);
+        case 2: return round_fn<2>(sample, gated, small, store);
+        case 4: return round_fn<4>(sample, gated, small, store);
+        case 8: return round_fn<8>(sample, gated, small, store);
+        case 16: return round_fn<16>(sample, gated, small, store);
         default: return nullptr;
     }
 }
 
-int round_max_coresident(int r, bool sample, bool gated, bool small) {
-    const void* fn = round_fn_r(r, sample, gated, small);
+int round_max_coresident(int r, bool sample, bool gated, bool small, bool store) {
+    const void* fn = round_fn_r(r, sample, gated, small, store);
     int per_cu = 0;
     if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kRoundThreads, 0) != hipSuccess) return 0;
     return per_cu * device_cu_count();
@@ -999,7 +1023,7 @@ int round_max_coresident(int r, bool sample, bool gated, bool small) {
 
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
                                hipEvent_t ev_end) {
-    const void* fn = round_fn_r(a.r, sample, gated, round_small_block(a.B));
+    const void* fn = round_fn_r(a.r, sample, gated, round_small_block(a.B), a.logits_out != nullptr);
     if (!fn) return hipErrorInvalidValue;
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
     RoundArgs copy = a;

@@ -11,7 +11,8 @@
 // wave arg-max.  Rows with k > 64 (small vocabularies only) are sorted whole in LDS by a bitonic network.
 // Pair scores: one workgroup per (row, position, block of 16 predecessors); the 16 gated predecessor
 // rows and each block of 16 candidate rows are staged in LDS as fp32 (16-byte loads), one thread per pair.
-// Walk: one wave per row, K serial picks over the precomputed rows, staged in LDS first.
+// Walk: every table row's pick resolved in parallel (greedy, or the whole-vocabulary draw restricted to the
+// candidates), then the path followed; tables too large for LDS are walked step by step from global memory.
 #include "internal.hpp"
 
 namespace dspark {
@@ -441,33 +442,81 @@ __global__ void __launch_bounds__(256) pair_score_mfma_kernel(SelectorArgs a) {
     }
 }
 
+// Sampling over a candidate set is the draw the whole-vocabulary head makes, restricted to the set: the
+// candidates are grouped by vocabulary block (id / 16, aligned blocks of 16 ids); block q's mass S_q (the sum of
+// its members' 2^(l c - M), c = log2(e) / T) races with its variate E_q = -log2 u(2 q) (largest S_q / E_q wins,
+// ties to the lower block), and inside the winner the id is drawn by inverse CDF over its members in ascending id
+// order with target u(2 q + 1) S_q, u(n) the uniform of fmix32(k2 ^ n).  The noise keys on vocabulary blocks,
+// never on candidate slots, so a set that holds the whole vocabulary draws what the full head draws.  Members
+// are visited in ascending id order through the step's sort permutation.
+struct SetDraw {
+    int sel;        // position (in ascending id order) of the drawn member
+    float total;    // sum of all members' masses
+};
+
+// ord[s]: slot of the s-th smallest id; ids[s]: that id; E[s], U2[s]: the race variate and target uniform of its
+// block; lmc(slot): l c of a slot; M: max of l c over the set.
+template <typename LC>
+__device__ __forceinline__ SetDraw draw_set(int n, const int32_t* ord, const int32_t* ids, const float* E,
+                                            const float* U2, LC lmc, float M) {
+    float total = 0.f, S = 0.f, bS = 0.f, bE = 1.f;
+    int beg = 0, bbeg = -1, bend = 0;
+    for (int s = 0; s < n; ++s) {
+        const float p = fast_exp2(lmc(ord[s]) - M);
+        total += p;
+        S += p;
+        if (s + 1 == n || (ids[s + 1] >> 4) != (ids[s] >> 4)) {  // end of a block's run
+            if (S > 0.f && (bbeg < 0 || S * bE > bS * E[s])) {
+                bS = S;
+                bE = E[s];
+                bbeg = beg;
+                bend = s + 1;
+            }
+            S = 0.f;
+            beg = s + 1;
+        }
+    }
+    if (bbeg < 0) return SetDraw{0, total};
+    const float target = fminf(U2[bbeg] * bS, __uint_as_float(__float_as_uint(bS) - 1u));
+    float cum = 0.f;
+    int sel = bbeg;
+    for (int s = bbeg; s + 1 < bend; ++s) {
+        cum += fast_exp2(lmc(ord[s]) - M);
+        sel += (cum <= target) ? 1 : 0;
+    }
+    return SetDraw{sel, total};
+}
+
 // One wave per row: K serial picks, reading the row's score tables and candidate ids from global memory (the
-// tables too large for the row-parallel walk below even with all of a workgroup's LDS).
+// tables too large for the row-parallel walk below even with all of a workgroup's LDS).  In sampling mode the
+// step's candidates are ranked by id in LDS and lane 0 makes the draw.
+constexpr int kWalkSortMax = 1024;
+
 __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
+    __shared__ int32_t s_ord[kWalkSortMax], s_ids[kWalkSortMax];
+    __shared__ float s_E[kWalkSortMax], s_U2[kWalkSortMax];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const size_t tstride = a.topk + (size_t)(a.K - 1) * a.topk * a.topk;
     const float* sc = a.scores + (size_t)b * tstride;
     const int32_t* cands = a.cand + (size_t)b * a.K * a.topk;
+    const float c = a.inv_t * kLog2e;
     int islot = 0;
     for (int t = 0; t < a.K; ++t) {
         const float* rowp = (t == 0) ? sc : sc + a.topk + ((size_t)(t - 1) * a.topk + islot) * a.topk;
         const int32_t* cand_t = cands + (size_t)t * a.topk;
-        const uint32_t k2 = a.sample ? noise_key2(a.k0, (uint32_t)b, (uint32_t)t) : 0u;
         float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
         int bi = 0x7FFFFFFF, bs = 0;
         for (int j = lane; j < a.topk; j += 64) {
             const float l = rowp[j];
-            const int c = cand_t[j];
-            const float tt = l * a.inv_t * kLog2e;
-            float key = a.sample ? tt + gumbel_log2_units(fmix32(k2 ^ (uint32_t)c)) : l;
-            if (beats(key, c, bk, bi)) {
-                bk = key;
-                bi = c;
+            const int cid = cand_t[j];
+            if (beats(l, cid, bk, bi)) {
+                bk = l;
+                bi = cid;
                 bl = l;
                 bs = j;
             }
-            lse_merge(m, s, tt, 1.0f);
+            lse_merge(m, s, l * c, 1.0f);
         }
         // reduce over the lanes that hold candidates (a 16-lane group when topk <= 16)
         const int span = a.topk <= 16 ? 16 : 64;
@@ -486,27 +535,52 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
             }
             lse_merge(m, s, om, oss);
         }
-        islot = bs;
+        // m is now the largest l c of the set (every lane), bs / bi / bl the greedy pick
+        if (a.sample) {
+            const uint32_t k2 = noise_key2(a.k0, (uint32_t)b, (uint32_t)t);
+            for (int j = lane; j < a.topk; j += 64) {
+                const int cid = cand_t[j];
+                int rank = 0;
+                for (int i = 0; i < a.topk; ++i) rank += cand_t[i] < cid ? 1 : 0;
+                const uint32_t q = (uint32_t)cid >> 4;
+                s_ord[rank] = j;
+                s_ids[rank] = cid;
+                s_E[rank] = neg_log2_uniform(fmix32(k2 ^ (2u * q)));
+                s_U2[rank] = hash_uniform(fmix32(k2 ^ (2u * q + 1u)));
+            }
+            __syncthreads();
+            if (lane == 0) {
+                const SetDraw d = draw_set(a.topk, s_ord, s_ids, s_E, s_U2, [&](int j) { return rowp[j] * c; }, m);
+                bs = s_ord[d.sel];
+                bi = s_ids[d.sel];
+                bl = rowp[bs];
+                s = d.total;
+            }
+            __syncthreads();
+        }
+        islot = __shfl(bs, 0);
         if (lane == 0) {
             a.tokens[(size_t)b * a.K + t] = bi;
-            if (a.logprobs) a.logprobs[(size_t)b * a.K + t] = bl * a.inv_t - (m + fast_log2(s)) * kLn2;
+            if (a.logprobs) a.logprobs[(size_t)b * a.K + t] = (bl * c - m - fast_log2(s)) * kLn2;
         }
     }
 }
 
 // The walk with every step's choice made in parallel.  A step's pick depends on the path only through the row
-// of the pair table it reads (the slot picked one step before); the row's keys (the scores, or the scores over T
-// plus the Gumbel noise of row b, step t and candidate id) and its log-sum-exp do not.  So the threads of the
-// workgroup take the table rows (the anchor row, then the topk rows of each later table) one per thread, and
+// of the pair table it reads (the slot picked one step before); the row's draw (greedy, or the block race with
+// noise of row b, step t and the candidates' vocabulary blocks) and its log-sum-exp do not.  So the threads of
+// the workgroup take the table rows (the anchor row, then the topk rows of each later table) one per thread, and
 // record each row's pick (slot, id, exact log-probability); one thread then follows the path, one LDS read per
 // step.  This replaces sixteen dependent cross-lane reductions by one pass over the rows.  Rows are staged with
-// a pitch of topk + 1 floats, so that the threads' reads of the same column fall in distinct banks.
+// a pitch of topk + 1 floats, so that the threads' reads of the same column fall in distinct banks.  In
+// sampling mode each step's candidates are first ranked by id (one thread per candidate) with their blocks'
+// race variates, which every row of that step's table shares.
 constexpr int kWalkThreads = 256;
 constexpr int kWalkLdsMax = 160 * 1024;  // a workgroup's LDS on gfx950
 
 size_t walk_rows_lds_bytes(int K, int topk) {
     const size_t rows = 1 + (size_t)(K - 1) * topk;
-    return 4 * (rows * (topk + 1) + (size_t)K * topk + 3 * rows);
+    return 4 * (rows * (topk + 1) + (size_t)K * topk + 3 * rows + 4 * (size_t)K * topk);
 }
 
 __global__ void __launch_bounds__(kWalkThreads) walk_rows_kernel(SelectorArgs a) {
@@ -523,6 +597,11 @@ __global__ void __launch_bounds__(kWalkThreads) walk_rows_kernel(SelectorArgs a)
     int32_t* pslot = cs + a.K * kk;                                           // per row: slot of its pick,
     int32_t* pid = pslot + rows;                                              // its id,
     float* plp = reinterpret_cast<float*>(pid + rows);                        // its log-probability
+    int32_t* sord = reinterpret_cast<int32_t*>(plp + rows);                   // [K][topk] slots by ascending id,
+    int32_t* sids = sord + a.K * kk;                                          // the ids,
+    float* sE = reinterpret_cast<float*>(sids + a.K * kk);                    // their blocks' race variates,
+    float* sU2 = sE + a.K * kk;                                               // and target uniforms
+    const float c = a.inv_t * kLog2e;
 
     // stage (one round trip: every thread's loads are issued before its LDS writes)
     constexpr int kBatch = 16;
@@ -541,30 +620,55 @@ __global__ void __launch_bounds__(kWalkThreads) walk_rows_kernel(SelectorArgs a)
     }
     for (int e = tid; e < a.K * kk; e += kWalkThreads) cs[e] = cands[e];
     __syncthreads();
+    if (a.sample) {
+        for (int e = tid; e < a.K * kk; e += kWalkThreads) {
+            const int t = e / kk, j = e - t * kk;
+            const int32_t* ct = cs + t * kk;
+            const int cid = ct[j];
+            int rank = 0;
+            for (int i = 0; i < kk; ++i) rank += ct[i] < cid ? 1 : 0;
+            const uint32_t k2 = noise_key2(a.k0, (uint32_t)b, (uint32_t)t);
+            const uint32_t q = (uint32_t)cid >> 4;
+            sord[t * kk + rank] = j;
+            sids[t * kk + rank] = cid;
+            sE[t * kk + rank] = neg_log2_uniform(fmix32(k2 ^ (2u * q)));
+            sU2[t * kk + rank] = hash_uniform(fmix32(k2 ^ (2u * q + 1u)));
+        }
+        __syncthreads();
+    }
 
     for (int row = tid; row < rows; row += kWalkThreads) {
         const int t = row == 0 ? 0 : 1 + (row - 1) / kk;  // the step whose choice this row makes
         const float* rp = ss + (size_t)row * pitch;
         const int32_t* ct = cs + t * kk;
-        const uint32_t k2 = a.sample ? noise_key2(a.k0, (uint32_t)b, (uint32_t)t) : 0u;
-        float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
+        float bk = -INFINITY, bl = 0.f, M = kMinFinite;
         int bi = 0x7FFFFFFF, bs = 0;
         for (int j = 0; j < kk; ++j) {
             const float l = rp[j];
-            const int c = ct[j];
-            const float tt = l * a.inv_t * kLog2e;
-            const float key = a.sample ? tt + gumbel_log2_units(fmix32(k2 ^ (uint32_t)c)) : l;
-            if (beats(key, c, bk, bi)) {
-                bk = key;
-                bi = c;
+            const int cid = ct[j];
+            if (beats(l, cid, bk, bi)) {
+                bk = l;
+                bi = cid;
                 bl = l;
                 bs = j;
             }
-            lse_merge(m, s, tt, 1.0f);
+            M = fmaxf(M, l * c);
+        }
+        float total;
+        if (a.sample) {
+            const SetDraw d = draw_set(kk, sord + t * kk, sids + t * kk, sE + t * kk, sU2 + t * kk,
+                                       [&](int j) { return rp[j] * c; }, M);
+            bs = sord[t * kk + d.sel];
+            bi = sids[t * kk + d.sel];
+            bl = rp[bs];
+            total = d.total;
+        } else {
+            total = 0.f;
+            for (int j = 0; j < kk; ++j) total += fast_exp2(rp[j] * c - M);
         }
         pslot[row] = bs;
         pid[row] = bi;
-        plp[row] = bl * a.inv_t - (m + fast_log2(s)) * kLn2;
+        plp[row] = (bl * c - M - fast_log2(total)) * kLn2;
     }
     __syncthreads();
 

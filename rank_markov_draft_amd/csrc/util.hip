@@ -7,6 +7,11 @@ namespace dspark {
 
 namespace {
 
+// p[0 .. n) = value (a kernel, not a memset, so that the call stays safe to capture in a graph)
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = value;
+}
+
 // dst[c, r] = src[r, c] for a rows x cols matrix of 2- or 4-byte elements, through 32 x 32 LDS tiles.
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ src, int rows, int cols, T* __restrict__ dst) {
@@ -58,6 +63,13 @@ hipError_t launch_stream_read(const void* a, size_t a_bytes, const void* b, size
     const int grid = 16 * device_cu_count();
     hipLaunchKernelGGL(stream_read_kernel<2>, dim3(grid), dim3(1024), 0, st, (const u32x4_t*)a, a_bytes / 16,
                        (const u32x4_t*)b, b_bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st) {
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)(blocks < 1024 ? (blocks ? blocks : 1) : 1024)), dim3(256), 0, st, p,
+                       value, n);
     return hipGetLastError();
 }
 

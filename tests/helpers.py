@@ -1,10 +1,11 @@
 """Shared helpers of the GPU parity tests: host <-> device marshalling and the comparison rules.
 
 Comparison rules (tolerances of the draft-calibration path):
-  * calibrated logits, pair scores and log-probabilities: |gpu - oracle| <= 1e-2;
-  * tokens: equal to the oracle's pick at every position whose oracle top-2 key margin is >= 2e-2;
-    positions with a smaller margin are flagged, and there either token is accepted (the oracle follows
-    the GPU's own path, so every later position is still compared under the same prefix);
+  * calibrated logits, pair scores and log-probabilities: |gpu - oracle| <= 1e-2 (tighter where stated);
+  * tokens: the oracle follows the GPU's own path (teacher forcing), so every position is compared under the
+    same prefix.  A GPU token equals the oracle's pick, or differs only where a perturbation of at most 1e-2 of
+    every key (greedy: logits; sampling: log-masses l / T) selects it (the oracle's ``reach``); such positions
+    have an oracle margin below 2e-2.  Differing tokens are counted and stay under a ceiling;
   * top-k candidate lists: identical ids in identical order.
 """
 import numpy as np
@@ -12,6 +13,7 @@ import torch
 
 LOGIT_TOL = 1e-2
 MARGIN_TOL = 2e-2
+MISMATCH_CEIL = 0.02  # at most this fraction of positions (and at least 2) may differ, each reachable
 
 
 def dev():
@@ -39,15 +41,25 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def check_draft(gpu_tok, gpu_lp, ref, *, lp_tol=LOGIT_TOL, margin_tol=MARGIN_TOL, what=""):
-    """ref: oracle output run with follow=gpu_tok.  Returns (n_flagged, n_mismatched_flagged)."""
+def check_draft(gpu_tok, gpu_lp, ref, *, lp_tol=LOGIT_TOL, mismatch_ceil=MISMATCH_CEIL, what=""):
+    """ref: oracle output run with follow=gpu_tok (it carries ``reach`` and ``lp_follow``).
+    Returns (n_flagged, n_mismatched) and prints them."""
+    assert "reach" in ref, "the oracle must follow the GPU's path"
     agree = gpu_tok == ref["tokens"]
-    flagged = ref["margins"] < margin_tol
-    bad = ~agree & ~flagged
-    assert not bad.any(), f"{what}: unflagged token mismatch at {np.argwhere(bad)[:8].tolist()}"
+    reach = ref["reach"] == 1
+    bad = ~agree & ~reach
+    assert not bad.any(), (f"{what}: GPU token not reachable from the oracle's logits at "
+                           f"{np.argwhere(bad)[:8].tolist()} (gpu {gpu_tok[bad][:8].tolist()}, "
+                           f"oracle {ref['tokens'][bad][:8].tolist()}, margin {ref['margins'][bad][:8].tolist()})")
+    flagged = ref["margins"] < MARGIN_TOL
+    n_mis = int((~agree).sum())
+    assert n_mis <= max(2, mismatch_ceil * agree.size), f"{what}: {n_mis} of {agree.size} tokens differ"
     if gpu_lp is not None:
         lp_ref = np.where(agree, ref["logprobs"], ref["lp_follow"])
         ok = ~np.isnan(lp_ref)
+        assert ok.all(), f"{what}: a GPU token outside the oracle's set"
         err = np.abs(gpu_lp[ok] - lp_ref[ok]).max() if ok.any() else 0.0
         assert err <= lp_tol, f"{what}: log-probability error {err}"
-    return int(flagged.sum()), int((~agree).sum())
+    print(f"[parity] {what}: {agree.size} positions, {int(flagged.sum())} flagged (margin < {MARGIN_TOL}), "
+          f"{n_mis} differ (all reachable)")
+    return int(flagged.sum()), n_mis

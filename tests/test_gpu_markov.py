@@ -7,6 +7,7 @@ workloads in the launch configuration the bench times and compare sampled rows.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle as O
 import synth as S
@@ -167,27 +168,31 @@ def serving():
     return S.workload("serving")
 
 
-def _full_draft_check(D, w, rows, mode, seed, H=None, Hd=None):
+def _full_draft_check(D, w, rows, mode, seed, H=None, Hd=None, what=""):
     tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), w2_layout=D.DSPARK_W2_VR,
                                     H=H, mode=mode, seed=seed)
     tok, lp = host(tok), host(lp)
     ref = O.markov_draft(w.U, w.W1, w.W2T, w.anchor, w2_layout=O.W2_VR, H=Hd, mode=mode, seed=seed, follow=tok,
                          rows=rows)
+    if rows is None:
+        return check_draft(tok, lp, ref, what=what)
     sub = {k: v[rows] for k, v in ref.items()}
-    return check_draft(tok[rows], lp[rows], sub)
+    return check_draft(tok[rows], lp[rows], sub, what=what)
 
 
-def test_full_serving_sampled_rows(D, serving):
-    """B=128, K=16, V=151936, r=256, sampling at T=1 (the block-race draw): every position of three rows."""
-    _full_draft_check(D, serving, [0, 77, 127], S.SAMPLE, serving.noise_seed)
+def test_full_serving_all_rows(D, serving):
+    """B=128, K=16, V=151936, r=256, sampling at T=1 (the measured workload and launch): every position of
+    every row against the oracle along the GPU's path."""
+    _full_draft_check(D, serving, None, S.SAMPLE, serving.noise_seed, what="serving sample")
 
 
-def test_full_serving_greedy_sampled_rows(D, serving):
-    """The serving shape with greedy picks (the bench's greedy line): every position of two rows."""
-    _full_draft_check(D, serving, [5, 100], S.GREEDY, 0)
+def test_full_serving_greedy_all_rows(D, serving):
+    """The serving shape with greedy picks (the bench's greedy line): every position of every row."""
+    _full_draft_check(D, serving, None, S.GREEDY, 0, what="serving greedy")
 
 
 def test_full_serving_logits_sampled_rows(D, serving):
+    """The per-position kernels' logits at the serving shape (teacher-forced predecessors)."""
     w = serving
     prev = w.anchor.copy()
     for k in (0, w.K // 2, w.K - 1):
@@ -198,9 +203,104 @@ def test_full_serving_logits_sampled_rows(D, serving):
         prev = (prev * 7 + 13) % w.V
 
 
+def test_full_serving_round_kernel_logits(D, serving):
+    """The whole-round kernel's own calibrated logits (its store variant: same contraction, same pick) at the
+    serving shape, sampling: tokens and log-probabilities are bit-identical to dspark_markov_draft's, and the
+    logits of positions 0, 7 and 15 of every row, at the GPU's own predecessors, match the oracle's."""
+    w = serving
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    kw = dict(w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_SAMPLE, seed=w.noise_seed)
+    tok, lp, logits = D.dspark_markov_draft_logits(*args, **kw)
+    tok2, lp2 = D.dspark_markov_draft(*args, **kw)
+    tok, lp = host(tok), host(lp)
+    assert np.array_equal(tok, host(tok2)) and np.array_equal(lp, host(lp2))
+    for k in (0, 7, w.K - 1):
+        got = host(logits[:, k].contiguous())
+        prev = w.anchor if k == 0 else tok[:, k - 1]
+        ref = O.markov_logits(w.U[:, k], w.W1, w.W2T, prev, w2_layout=O.W2_VR)
+        err = np.abs(got - ref).max()
+        assert err <= 1e-3, (k, err)
+    del logits
+
+
+ROUND_SHAPES = [(8, 3, 3000, 256), (3, 2, 1000, 32), (130, 2, 776, 64), (128, 3, 4096, 256), (40, 2, 2000, 128)]
+
+
+@pytest.mark.parametrize("shape", ROUND_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d" % s)
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+def test_round_kernel_logits(D, shape, mode, gated):
+    """Every calibrated logit the whole-round kernel computes, at every position, against the oracle's at the
+    GPU's own predecessors: small and full row blocks, ragged vocabulary tails, several ranks, both picks, the
+    gate.  Strong weights, so that a dropped or misplaced bias term shows."""
+    B, K, V, r = shape
+    w = S.strong("serving", B=B, K=K, V=V, r=r, mode=mode)
+    H = _rand_H(B, K, r, seed=9) if gated else None
+    tok, lp, logits = D.dspark_markov_draft_logits(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor),
+                                                   H=None if H is None else t_f32(H), mode=mode, seed=13,
+                                                   temperature=0.9)
+    tok, lp, got = host(tok), host(lp), host(logits)
+    for k in range(K):
+        prev = w.anchor if k == 0 else tok[:, k - 1]
+        ref = O.markov_logits(w.U[:, k], w.W1, w.W2T, prev, w2_layout=O.W2_VR,
+                              Hk=None if H is None else H[:, k].astype(np.float64))
+        err = np.abs(got[:, k] - ref).max()
+        assert err <= (LOGIT_TOL if gated else 1e-3), (k, err)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, H=None if H is None else H.astype(np.float64), mode=mode,
+                         seed=13, temperature=0.9, follow=tok)
+    check_draft(tok, lp, ref, what=f"round logits {shape}")
+
+
+def test_round_logits_rejects_other_paths(D):
+    """The validation call exists for the whole-round kernel only: an fp32-weight shape is refused."""
+    w = S.strong("serving", B=2, K=2, V=300, r=16, wdtype=S.F32)
+    with pytest.raises(D.DsparkError) as e:
+        D.dspark_markov_draft_logits(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    assert e.value.status == D.DSPARK_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("cfg,mode", [("batch1", S.GREEDY), ("serving", S.SAMPLE)])
+def test_gate_ones_equals_ungated_at_full_shapes(D, cfg, mode):
+    """H = 1 makes the gated head the ungated one (equivalence page, "The equivalence: remove the gate"), at the
+    batch-1 (greedy) and serving (sampling) shapes: the gated and ungated kernels draft the same tokens.  At the
+    serving shape both run the same consumer arrangement, so log-probabilities agree bit for bit too."""
+    w = S.workload(cfg)
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    a = D.dspark_markov_draft(*args, mode=mode, seed=w.noise_seed)
+    ones = torch.ones((w.B, w.K, w.r), dtype=torch.float32, device="cuda")
+    b = D.dspark_markov_draft(*args, mode=mode, seed=w.noise_seed, H=ones)
+    assert np.array_equal(host(a[0]), host(b[0]))
+    if cfg == "serving":
+        assert np.array_equal(host(a[1]), host(b[1]))
+    else:
+        np.testing.assert_allclose(host(a[1]), host(b[1]), rtol=0, atol=1e-5)
+
+
 def test_full_batch1_greedy(D):
     w = S.workload("batch1")
-    _full_draft_check(D, w, [0], S.GREEDY, 0)
+    _full_draft_check(D, w, None, S.GREEDY, 0, what="batch-1 greedy")
+
+
+def test_device_timeout_is_reported(D):
+    """Failure path of the whole-round kernel, forced from the host: a spin limit of one sleep makes its bounded
+    waits give up (every wait still ends, so the kernel exits normally).  The status call then reports
+    DSPARK_EDEVICE; with the default limit restored the same workspace drafts correctly and reports OK."""
+    w = S.workload("serving", B=16, K=3, V=4096, r=64, mode=S.GREEDY)
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    nbytes = D.dspark_markov_workspace_bytes(w.B, w.K, w.V, w.r, D.DSPARK_BF16, D.DSPARK_W2_VR)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    D.dspark_set_spin_limit(1)
+    try:
+        D.dspark_markov_draft(*args, workspace=ws)
+        status = D.dspark_markov_status(ws, w.B, w.K)
+    finally:
+        D.dspark_set_spin_limit(0)
+    assert status == D.DSPARK_EDEVICE
+    tok, lp = D.dspark_markov_draft(*args, workspace=ws)
+    assert D.dspark_markov_status(ws, w.B, w.K) == D.DSPARK_OK
+    tok, lp = host(tok), host(lp)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, follow=tok)
+    check_draft(tok, lp, ref, what="after a forced timeout")
 
 
 @pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])

@@ -4,7 +4,7 @@ import pytest
 
 import oracle as O
 import synth as S
-from helpers import LOGIT_TOL, MARGIN_TOL, check_draft, host, t_f32, t_i32, t_w
+from helpers import LOGIT_TOL, check_draft, host, t_f32, t_i32, t_w
 
 pytestmark = pytest.mark.gpu
 
@@ -51,9 +51,22 @@ def test_topk_large_k_small_vocab(D, V, k):
 SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 96, 16, 16, S.F32),
               (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16), (3, 3, 2000, 32, 32, S.BF16),
               (2, 3, 5000, 64, 64, S.BF16),
+              # r = 256 (the measured rank: the matrix-core pair scores loop over several rank batches)
+              (4, 4, 3000, 256, 16, S.BF16),
               # K = 16 with k = 32 (the row-parallel walk with more than 64 KB of LDS) and k = 64 (tables
               # beyond the workgroup's LDS, walked step by step from global memory)
               (2, 16, 1000, 32, 32, S.BF16), (2, 16, 1000, 32, 64, S.BF16)]
+
+
+def _restricted_check(D, w, A, Bemb, H, cand, tok, lp, mode, seed, T, what, rows=None):
+    """The walk's tokens against the head restricted to the same candidates, along the GPU's own path."""
+    ref = O.markov_restricted(w.U, A, Bemb, w.anchor, cand, w2_layout=O.W2_VR,
+                              H=None if H is None else H.astype(np.float64), mode=mode, seed=seed, temperature=T,
+                              follow=tok, rows=rows)
+    if rows is not None:
+        ref = {k: v[rows] for k, v in ref.items()}
+        tok, lp = tok[rows], None if lp is None else lp[rows]
+    return check_draft(tok, lp, ref, what=what)
 
 
 @pytest.mark.parametrize("shape", SEL_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d-k%d" % s[:5])
@@ -73,64 +86,50 @@ def test_selector_parity(D, shape, mode, gated):
     assert np.array_equal(cand, ref["cand"])
     tol = LOGIT_TOL if gated else 1e-3
     assert np.abs(scores - ref["tables"]).max() <= tol
-    # walk: along the GPU's own path the oracle's pick agrees wherever its margin is not tiny
-    ref_r = O.markov_restricted(w.U, A, Bemb, w.anchor, cand, w2_layout=O.W2_VR,
-                                H=None if H is None else H.astype(np.float64), mode=mode, seed=77, temperature=T)
-    flagged = ref_r["margins"] < MARGIN_TOL
-    agree = tok == ref_r["tokens"]
-    first_bad = np.where(~agree & ~flagged)
-    # compare each row up to its first flagged divergence (a divergence changes all later predecessors)
-    for b in range(B):
-        for t in range(K):
-            if tok[b, t] != ref_r["tokens"][b, t]:
-                assert flagged[b, t], (b, t, first_bad)
-                break
-            assert abs(lp[b, t] - ref_r["logprobs"][b, t]) <= tol
+    _restricted_check(D, w, A, Bemb, H, cand, tok, lp, mode, 77, T, f"selector {shape} {mode} gated={gated}")
 
 
-def test_selector_topk_V_equals_full_head(D):
-    """top-k = V: the truncated execution is the full-vocabulary Markov head.  Greedy: the same picks as the
-    full head, the oracle's and the library's.  Sampling: the candidate set is the whole vocabulary, drawn
-    by Gumbel-max per candidate (the full head draws by the block race: the same distribution, other
-    noise), so the reference is the head restricted to the whole vocabulary."""
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+def test_selector_topk_V_equals_full_head(D, mode):
+    """top-k = V on the tiny workload (V = 512): the truncated execution is the full-vocabulary head, in both
+    modes.  The Selector's tokens are checked against the oracle's full head (not a restricted one) along the
+    Selector's own path, and so are the full head's tokens; in sampling mode both draw with the same noise
+    (keyed on vocabulary blocks), so the two GPU paths draft the same tokens wherever no near-tie separates them."""
     w = S.strong("tiny")
-    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), topk=w.V, mode=S.GREEDY, seed=3)
+    T = 0.9 if mode == S.SAMPLE else 1.0
+    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), topk=w.V, mode=mode, seed=3,
+                                  temperature=T)
     tok, lp = host(res["tokens"]), host(res["logprobs"])
-    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=S.GREEDY, seed=3, follow=tok)
-    check_draft(tok, lp, ref)
+    ref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=3, temperature=T, follow=tok)
+    check_draft(tok, lp, ref, what=f"selector top-k=V {mode}")
     gtok, glp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2), t_i32(w.anchor), w2_layout=D.DSPARK_W2_RV,
-                                      mode=S.GREEDY, seed=3)
-    gtok = host(gtok)
-    agree_until = np.cumprod(gtok == tok, axis=1).astype(bool)
-    assert agree_until[:, 0].all() or (ref["margins"][:, 0] < MARGIN_TOL).all()
-    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), topk=w.V, mode=S.SAMPLE, seed=3)
-    tok, lp = host(res["tokens"]), host(res["logprobs"])
-    cand = np.broadcast_to(np.arange(w.V, dtype=np.int32), (w.B, w.K, w.V))
-    ref = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand, mode=S.SAMPLE, seed=3)
-    # the restricted oracle runs its own path: compare up to the first flagged position of each row
+                                      mode=mode, seed=3, temperature=T)
+    gtok, glp = host(gtok), host(glp)
+    gref = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=3, temperature=T, follow=gtok)
+    check_draft(gtok, glp, gref, what=f"full head {mode}")
+    # the two GPU paths share their predecessors up to their first difference, which needs a near-tie there
     for b in range(w.B):
-        for t in range(w.K):
-            if ref["margins"][b, t] < MARGIN_TOL:
-                break
-            assert tok[b, t] == ref["tokens"][b, t]
-            assert abs(lp[b, t] - ref["logprobs"][b, t]) <= 1e-2
+        diff = np.nonzero(tok[b] != gtok[b])[0]
+        if diff.size:
+            t = int(diff[0])
+            assert min(ref["margins"][b, t], gref["margins"][b, t]) < 2e-2, (b, t)
 
 
-def test_full_selector_sampled_rows(D):
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+def test_full_selector_all_rows(D, mode):
+    """B=128, K=16, V=151936, r=256, top-16 (the measured Selector workload): every row's candidates exactly,
+    the pair tables of sampled rows, and every row's walk against the restricted head along the GPU's path."""
     w = S.workload("selector")
-    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), topk=16, want_cand=True)
-    tok, cand = host(res["tokens"]), host(res["cand"])
+    T = 1.0
+    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), topk=16, mode=mode,
+                                  seed=w.noise_seed, temperature=T, want_cand=True, want_scores=True)
+    tok, lp, cand, scores = (host(res[k]) for k in ("tokens", "logprobs", "cand", "scores"))
+    ridx, _ = O.topk(w.U, 16)
+    assert np.array_equal(cand, ridx)
     rows = [0, 50, 127]
-    for b in rows:
-        ridx, _ = O.topk(w.U[b], 16)
-        assert np.array_equal(cand[b], ridx)
-    ref = O.selector_draft(w.U, w.W1, w.W2T, w.anchor, topk=16, rows=rows)
-    flagged = ref["margins"][rows] < MARGIN_TOL
-    for i, b in enumerate(rows):
-        for t in range(w.K):
-            if tok[b, t] != ref["tokens"][b, t]:
-                assert flagged[i, t]
-                break
+    ref = O.selector_draft(w.U, w.W1, w.W2T, w.anchor, topk=16, mode=mode, seed=w.noise_seed, rows=rows)
+    assert np.abs(scores[rows] - ref["tables"][rows]).max() <= 1e-3
+    _restricted_check(D, w, w.W1, w.W2T, None, cand, tok, lp, mode, w.noise_seed, T, f"full selector {mode}")
 
 
 # -------------------------------------------------------------------------------------------- gate
@@ -148,25 +147,22 @@ def test_gate_parity(D, rows, Dm, r):
 
 
 def test_full_gated_workload(D):
-    """B=64, K=16, V=129280, r=256, D=4096: gate for the whole block, then the gated full-vocabulary head
-    and its top-16 Selector form, sampled rows against the oracle (which computes its own gate)."""
+    """B=64, K=16, V=129280, r=256, D=4096: the gate for the whole block, then the gated full-vocabulary head
+    and its top-16 Selector form, every row against the oracle (which computes its own gate)."""
     w = S.workload("gated")
     H = D.dspark_gate(t_w(w.h), t_w(w.Wg))
     Hh = host(H)
-    rows = [0, 31, 63]
-    Href = O.gate(w.h[rows], w.Wg)
-    assert np.abs(Hh[rows] - Href).max() <= 1e-3
-    Hd = np.zeros((w.B, w.K, w.r))
-    Hd[rows] = Href
+    Href = O.gate(w.h, w.Wg)
+    assert np.abs(Hh - Href).max() <= 1e-3
     tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), H=H)
     tok, lp = host(tok), host(lp)
-    ref = O.markov_draft(w.U, w.W1, w.W2T, w.anchor, w2_layout=O.W2_VR, H=Hd, follow=tok, rows=rows)
-    check_draft(tok[rows], lp[rows], {k: v[rows] for k, v in ref.items()})
-    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), H=H, topk=16, want_cand=True)
-    stok, cand = host(res["tokens"]), host(res["cand"])
-    sref = O.markov_restricted(w.U, w.W1, w.W2T, w.anchor, cand, w2_layout=O.W2_VR, H=Hd, rows=rows)
-    for b in rows:
-        for t in range(w.K):
-            if stok[b, t] != sref["tokens"][b, t]:
-                assert sref["margins"][b, t] < MARGIN_TOL
-                break
+    ref = O.markov_draft(w.U, w.W1, w.W2T, w.anchor, w2_layout=O.W2_VR, H=Href, follow=tok)
+    check_draft(tok, lp, ref, what="gated head")
+    res = D.dspark_selector_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor), H=H, topk=16, want_cand=True,
+                                  want_scores=True)
+    stok, slp, cand, scores = (host(res[k]) for k in ("tokens", "logprobs", "cand", "scores"))
+    rows = [0, 31, 63]
+    sref = O.selector_draft(w.U, w.W1, w.W2T, w.anchor, H=Href, topk=16, rows=rows)
+    assert np.array_equal(cand[rows], sref["cand"][rows])
+    assert np.abs(scores[rows] - sref["tables"][rows]).max() <= LOGIT_TOL
+    _restricted_check(D, w, w.W1, w.W2T, Href, cand, stok, slp, S.GREEDY, 0, 1.0, "gated selector")

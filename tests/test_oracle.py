@@ -413,16 +413,101 @@ def test_selector_equals_markov_restricted_to_its_candidates(mode, gated):
     assert np.all(np.isin(sel["tokens"], cand.reshape(B, -1)))
 
 
-@pytest.mark.parametrize("mode", [O.GREEDY])
+@pytest.mark.parametrize("mode", [O.GREEDY, O.SAMPLE])
 def test_selector_with_topk_V_is_the_full_head(mode):
-    """Special case: with the candidate set equal to the whole vocabulary the truncation is exact.
-    (Greedy only: a candidate set is sampled by Gumbel-max per candidate, the whole vocabulary by the
-    block race; both draw from the same softmax, with different noise.)"""
-    w = S.workload("tiny", V=64)
-    sel = O.selector_draft(w.U, w.W1, np.ascontiguousarray(w.W2.T), w.anchor, topk=w.V, mode=mode, seed=5)
-    full = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=5)
+    """Special case (spec: top-k = V on a tiny vocabulary): with the candidate set equal to the whole
+    vocabulary the truncation is exact, in both modes and bit for bit: the sampling draw is one definition
+    over a set of ids (race between vocabulary blocks, noise keyed on the block, sums in ascending id order),
+    so a candidate list in any slot order that holds every id draws what the whole vocabulary draws."""
+    w = S.strong("tiny", V=64, K=4)
+    sel = O.selector_draft(w.U, w.W1, np.ascontiguousarray(w.W2.T), w.anchor, topk=w.V, mode=mode, seed=5,
+                           temperature=0.8)
+    full = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=5, temperature=0.8)
     assert np.array_equal(sel["tokens"], full["tokens"])
-    np.testing.assert_allclose(sel["logprobs"], full["logprobs"], rtol=0, atol=1e-12)
+    assert np.array_equal(sel["logprobs"], full["logprobs"])
+    assert np.array_equal(sel["margins"], full["margins"])
+    # the candidate order is (U desc, id asc), not id order, so the equality is not a trivial one
+    assert not np.array_equal(sel["cand"][0, 0], np.arange(w.V))
+
+
+def _one_row_restricted(U_row, cand_row, mode, seed, T, n):
+    """The restricted head at one position (W2 = 0, so the logits are U) for n replicated rows."""
+    V = U_row.shape[0]
+    r = 2
+    U = np.broadcast_to(U_row, (n, 1, V)).copy()
+    cand = np.broadcast_to(np.asarray(cand_row, np.int32), (n, 1, len(cand_row))).copy()
+    return O.markov_restricted(U, np.zeros((V, r), np.float32), np.zeros((r, V), np.float32),
+                               np.zeros(n, np.int32), cand, mode=mode, seed=seed, temperature=T)
+
+
+@pytest.mark.parametrize("T", [0.5, 2.0])
+def test_restricted_draw_one_member_per_block_is_gumbel_max(T):
+    """Special case: when every candidate sits in a vocabulary block of its own, the race between blocks is
+    the textbook Gumbel-max over the candidates, argmax_c l_c / T + G(seed, row, pos, 2 (c div 16)), with G
+    the noise function pinned above (published hash vectors, Gumbel moments).  numpy argmax over the same
+    keys, per row; at T != 1 a key of l T instead of l / T, or noise subtracted instead of added, differs."""
+    rng = np.random.default_rng(60)
+    V, n = 400, 512
+    blocks = rng.choice(V // 16, 12, replace=False)
+    cand = (16 * blocks + rng.integers(0, 16, blocks.size)).astype(np.int32)
+    rng.shuffle(cand)
+    u = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    res = _one_row_restricted(u, cand, O.SAMPLE, 41, T, n)
+    l = u[cand].astype(np.float64)
+    for row in range(n):
+        g = np.array([O.gumbel(41, row, 0, 2 * int(c // 16)) for c in cand])
+        assert res["tokens"][row, 0] == cand[int(np.argmax(l / T + g))]
+    p = special.softmax(l / T)
+    lp = np.log(p)[[int(np.nonzero(cand == t)[0][0]) for t in res["tokens"][:, 0]]]
+    np.testing.assert_allclose(res["logprobs"][:, 0], lp, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_restricted_draw_inside_one_block_is_inverse_transform(T):
+    """Special case: when every candidate sits in one vocabulary block q, the race has one entrant and the
+    draw is inverse transform sampling of softmax(l / T) over the candidates in ascending id order with the
+    uniform of noise id 2q + 1: numpy searchsorted over the cumulative masses (first inclusive prefix above u
+    times the total), whatever the slot order of the candidate list."""
+    rng = np.random.default_rng(61)
+    V, n = 200, 256
+    q = 7
+    cand = (16 * q + rng.choice(16, 9, replace=False)).astype(np.int32)
+    u = (rng.standard_normal(V) * 2.0).astype(np.float32)
+    res = _one_row_restricted(u, cand, O.SAMPLE, 5, T, n)
+    ids = np.sort(cand)
+    z = u[ids].astype(np.float64) / T
+    w = np.exp(z - z.max())
+    cum = np.cumsum(w)
+    for row in range(n):
+        j = int(np.searchsorted(cum, O.noise_uniform(5, row, 0, 2 * q + 1) * cum[-1], side="right"))
+        assert res["tokens"][row, 0] == ids[min(j, ids.size - 1)]
+
+
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_restricted_draw_follows_softmax_over_the_set(T):
+    """Statistics: a candidate set spread over blocks with one, several and all but one of their ids, one
+    row replicated over 2^16 rows (the noise keys on the row): the draw frequencies follow softmax(l / T)
+    over the set (chi-square), and the reported log-probability is the exact log-softmax over the set.  A
+    temperature applied as l T, noise with the wrong sign, block masses without their variates or a
+    reversed inverse CDF each fail."""
+    rng = np.random.default_rng(62)
+    V, n = 160, 1 << 16
+    cand = np.concatenate([[5], 16 * 2 + np.arange(4), 16 * 5 + np.delete(np.arange(16), 3), [16 * 9 + 11]])
+    cand = rng.permutation(cand).astype(np.int32)
+    u = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    u[16 * 5: 16 * 6] -= 1.5  # the big block is not the obvious winner
+    res = _one_row_restricted(u, cand, O.SAMPLE, 0xBEEF, T, n)
+    l = u[cand].astype(np.float64)
+    p = special.softmax(l / T)
+    order = np.argsort(cand)  # ascending ids
+    counts = np.bincount(np.searchsorted(cand[order], res["tokens"][:, 0]), minlength=cand.size)
+    expect = p[order] * n
+    keep = expect > 5
+    chi2 = ((counts[keep] - expect[keep]) ** 2 / expect[keep]).sum()
+    assert stats.chi2.sf(chi2, keep.sum() - 1) > 1e-4
+    lp_of = dict(zip(cand.tolist(), np.log(p).tolist()))
+    want = np.array([lp_of[int(t)] for t in res["tokens"][:, 0]])
+    np.testing.assert_allclose(res["logprobs"][:, 0], want, rtol=0, atol=1e-12)
 
 
 @pytest.mark.parametrize("k", [2, 4, 8, 16])
@@ -478,12 +563,14 @@ def test_rows_are_independent_and_restricted_full_sets_is_full():
     one = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=O.SAMPLE, seed=7, rows=[2])
     assert np.array_equal(one["tokens"][2], full["tokens"][2])
     assert np.all(one["tokens"][[0, 1, 3]] == -1)
-    # greedy: the head restricted to the whole vocabulary is the head
-    fullg = O.markov_draft(w.U, w.W1, w.W2, w.anchor)
-    cand = np.broadcast_to(np.arange(w.V, dtype=np.int32), (w.B, w.K, w.V))
-    res = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand)
-    assert np.array_equal(res["tokens"], fullg["tokens"])
-    np.testing.assert_allclose(res["logprobs"], fullg["logprobs"], rtol=0, atol=1e-12)
+    # the head restricted to the whole vocabulary (as a shuffled candidate list) is the head, in both modes
+    cand = np.stack([np.random.default_rng(i).permutation(w.V) for i in range(w.B * w.K)]).astype(np.int32)
+    cand = cand.reshape(w.B, w.K, w.V)
+    for mode in (O.GREEDY, O.SAMPLE):
+        f = O.markov_draft(w.U, w.W1, w.W2, w.anchor, mode=mode, seed=7)
+        res = O.markov_restricted(w.U, w.W1, w.W2, w.anchor, cand, mode=mode, seed=7)
+        assert np.array_equal(res["tokens"], f["tokens"])
+        assert np.array_equal(res["logprobs"], f["logprobs"])
 
 
 def test_shift_invariance():
@@ -499,6 +586,58 @@ def test_shift_invariance():
         assert ok.mean() > 0.9
         assert np.array_equal(a["tokens"][ok], b["tokens"][ok])
         np.testing.assert_allclose(a["logprobs"], b["logprobs"], rtol=0, atol=1e-3)
+
+
+# -------------------------------------------------------------------------------------- reachability
+
+@pytest.mark.parametrize("mode,T", [(O.GREEDY, 1.0), (O.SAMPLE, 1.0), (O.SAMPLE, 0.6)])
+def test_reach_accepts_every_token_a_small_perturbation_selects(mode, T):
+    """Brute force: the parity rule accepts a GPU token that differs from the oracle's pick only when a
+    perturbation of at most eps of every key (greedy: l; sampling: l / T) selects it.  On positions whose
+    margin is below 2 eps, random and corner perturbations (|delta| <= 0.98 eps) of the logits are applied and
+    the position drawn again (same row, position and noise): every token so drawn must be declared reachable
+    at the unperturbed logits.  The declared set stays small (it is not "anything goes"), and the
+    perturbations do change some picks (the check is not vacuous)."""
+    eps = O.REACH_EPS
+    rng = np.random.default_rng(70 + int(10 * T) + mode)
+    V, r = 48, 2
+    W1, W2 = np.zeros((V, r), np.float32), np.zeros((r, V), np.float32)
+    changed, checked, sizes = 0, 0, []
+    for seed in range(4000):
+        u = (rng.standard_normal(V) * (0.1 if mode == O.GREEDY else 1.0)).astype(np.float32)
+        U = u[None, None, :]
+        base = O.markov_draft(U, W1, W2, np.zeros(1, np.int32), mode=mode, seed=seed, temperature=T)
+        if not base["margins"][0, 0] < 2 * eps:
+            continue
+        checked += 1
+        reach = [int(O.markov_draft(U, W1, W2, np.zeros(1, np.int32), mode=mode, seed=seed, temperature=T,
+                                    follow=np.array([[f]], np.int32))["reach"][0, 0]) for f in range(V)]
+        assert reach[base["tokens"][0, 0]] == 1
+        sizes.append(sum(reach))
+        for j in range(48):
+            d = rng.uniform(-1, 1, V) if j % 2 else rng.choice([-1.0, 1.0], V)
+            Up = (u.astype(np.float64) + 0.98 * eps * T * d).astype(np.float32)[None, None, :]
+            t2 = int(O.markov_draft(Up, W1, W2, np.zeros(1, np.int32), mode=mode, seed=seed, temperature=T)["tokens"][0, 0])
+            changed += t2 != base["tokens"][0, 0]
+            assert reach[t2] == 1, (seed, t2, base["tokens"][0, 0], base["margins"][0, 0])
+        if checked >= 60:
+            break
+    assert checked >= 20 and changed > 0
+    assert np.mean(sizes) < 6 and max(sizes) < V // 2, sizes
+
+
+def test_reach_is_exact_for_greedy_and_rejects_far_tokens():
+    """Closed form for greedy: a token is reachable exactly when its logit is within 2 eps of the largest."""
+    rng = np.random.default_rng(80)
+    V, r, eps = 64, 2, O.REACH_EPS
+    u = (rng.standard_normal(V) * 0.03).astype(np.float32)
+    U = u[None, None, :]
+    W1, W2 = np.zeros((V, r), np.float32), np.zeros((r, V), np.float32)
+    follow = np.arange(V, dtype=np.int32)[:, None]
+    res = O.markov_draft(np.repeat(U, V, 0), W1, W2, np.zeros(V, np.int32), follow=follow)
+    want = u.astype(np.float64) >= u.astype(np.float64).max() - 2 * eps
+    assert np.array_equal(res["reach"][:, 0].astype(bool), want)
+    assert 1 < want.sum() < V
 
 
 # -------------------------------------------------------------------------------------- confidence head
@@ -592,6 +731,15 @@ def test_schedule_hand_example():
     sps = np.where(B > 0, 1.0 / np.maximum(B, 1), 0).astype(np.float32)
     lengths, theta = O.schedule_greedy(a, sps)
     assert np.array_equal(lengths, [0, 0]) and theta == pytest.approx(1.0, rel=1e-7)
+
+
+def test_schedule_stops_when_theta_does_not_strictly_increase():
+    """The stop rule of the greedy ("admit them while Theta increases", read as strictly increases): with a flat
+    SPS an extension of survival 0 leaves Theta unchanged and is not admitted, nor is anything after it."""
+    a = np.array([[0.5, 0.0, 0.0]], np.float32)
+    sps = np.ones(1 * 4 + 1, np.float32)
+    lengths, theta = O.schedule_greedy(a, sps)
+    assert lengths.tolist() == [1] and theta == 1.5
 
 
 @pytest.mark.parametrize("seed", range(6))
