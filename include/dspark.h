@@ -127,6 +127,24 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         size_t workspace_bytes, void* stream);
 
 /*
+ * dspark_markov_draft for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same computation and kernels, with no workspace
+ * argument.  The scratch is a file-scope device array of the library, dspark_markov_noalloc_max_bytes()
+ * = 16 MiB per device, held until the process ends; this call neither allocates nor frees.  Every call on a
+ * device shares that device's array, so calls that overlap in time on one device (other streams, other host
+ * threads) race and give wrong results; calls in order on one stream are safe.  The kernels clear what must
+ * start at zero themselves.  Shapes whose workspace (dspark_markov_workspace_bytes) exceeds the array return
+ * DSPARK_EUNSUPPORTED (B = 128, K = 16 needs about 11 MB on a 256-CU device), and so does a bf16 W2 stored
+ * [r, V] (its transposed copy would not fit: use DSPARK_W2_VR, or dspark_pack_w2 once).  A position that fails
+ * on the device is marked as in dspark_markov_draft (tokens -1, logprobs NaN); dspark_markov_status, which reads
+ * a caller's workspace, does not apply to this call.
+ */
+size_t dspark_markov_noalloc_max_bytes(void);
+int dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                                const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                                uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* stream);
+
+/*
  * Device-side status of the last dspark_markov_draft* call made with this workspace (and these B, K) on
  * `stream`: waits for the stream (this call synchronises the host), then returns DSPARK_EDEVICE if a bounded
  * wait of the whole-round kernel gave up (tokens -1 and logprobs NaN where it failed), DSPARK_OK otherwise.

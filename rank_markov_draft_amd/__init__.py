@@ -48,6 +48,9 @@ def _load_lib():
         "dspark_markov_draft_logits": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp,
                                         sz, vp], i32),
         "dspark_markov_status": ([vp, sz, i32, i32, vp], i32),
+        "dspark_markov_noalloc_max_bytes": ([], sz),
+        "dspark_markov_draft_noalloc": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp],
+                                        i32),
         "dspark_set_spin_limit": ([ctypes.c_uint32], None),
         "dspark_markov_draft_confidence": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, i32, vp,
                                             vp, vp, vp, vp, vp, sz, vp], i32),
@@ -179,6 +182,27 @@ def dspark_markov_draft_logits(U, W1, W2, anchor, *, w2_layout=DSPARK_W2_VR, H=N
                                                mode, seed, float(temperature), _p(tokens), _p(logprobs), _p(logits),
                                                _p(ws), wsb, _stream(stream)), "dspark_markov_draft_logits")
         return tokens, logprobs, logits
+
+
+def dspark_markov_draft_noalloc(U, W1, W2, anchor, tokens, logprobs, *, w2_layout=DSPARK_W2_VR, H=None,
+                                mode=DSPARK_GREEDY, seed=0, temperature=1.0, stream=None):
+    """dspark_markov_draft with the library's own scratch array instead of a workspace: the caller passes the
+    outputs (tokens [B,K] int32, logprobs [B,K] fp32 or None); nothing is allocated."""
+    _dev(U, "U", torch.float32, 3)
+    B, K, V = U.shape
+    _dev(W1, "W1", (torch.bfloat16, torch.float32), 2)
+    _dev(W2, "W2", W1.dtype, 2)
+    r = W1.shape[1]
+    _dev(anchor, "anchor", torch.int32, 1)
+    _dev(tokens, "tokens", torch.int32, 2)
+    if logprobs is not None:
+        _dev(logprobs, "logprobs", torch.float32, 2)
+    if H is not None:
+        _dev(H, "H", torch.float32, 3)
+    _check(_lib.dspark_markov_draft_noalloc(_p(U), _p(W1), _p(W2), _wdtype(W1), w2_layout, _p(anchor), _p(H), B, K, V,
+                                            r, mode, seed, float(temperature), _p(tokens), _p(logprobs),
+                                            _stream(stream)), "dspark_markov_draft_noalloc")
+    return tokens, logprobs
 
 
 def dspark_markov_status(workspace, B, K, *, stream=None):

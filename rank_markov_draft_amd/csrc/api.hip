@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dspark.h"
@@ -330,6 +331,36 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
     return DSPARK_OK;
 }
 
+// Scratch of the entry point that allocates nothing (dspark_markov_draft_noalloc): one array per device, held
+// until the process ends.  Host code never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address); it resolves the device address once per device with hipGetSymbolAddress and uses
+// that pointer.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch array (resolved once per device, with that device current), or
+// null with the reason in g_err.
+void* scratch_ptr() {
+    static std::mutex mu;
+    static void* ptrs[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        fail(DSPARK_EDEVICE, "no current device");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            device_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 }  // namespace
 }  // namespace dspark
 
@@ -383,6 +414,27 @@ int dspark_markov_draft(const float* U, const void* W1, const void* W2, int wdty
                         void* stream) {
     return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
                              logprobs, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+size_t dspark_markov_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, int wdtype, int w2_layout,
+                                const int32_t* anchor, const float* H, int B, int K, int V, int r, int mode,
+                                uint64_t seed, float temperature, int32_t* tokens, float* logprobs, void* stream) {
+    g_err[0] = 0;
+    int rc = check_common(W1, W2, wdtype, w2_layout, B, V, r, mode, temperature);
+    if (rc) return rc;
+    if (K <= 0) return fail(DSPARK_EINVAL, "K must be positive");
+    if (w2_layout == DSPARK_W2_RV && mfma_eligible(wdtype, r))
+        return fail(DSPARK_EUNSUPPORTED, "the allocation-free draft needs W2 as [V, r] (DSPARK_W2_VR) for bf16 weights");
+    const size_t need = markov_ws_bytes(B, K, V, r, wdtype, w2_layout, true);
+    if (need > kScratchBytes)
+        return fail(DSPARK_EUNSUPPORTED, "B=%d K=%d needs %zu bytes of scratch, more than the %zu the library holds", B, K,
+                    need, kScratchBytes);
+    void* ws = scratch_ptr();
+    if (!ws) return DSPARK_EDEVICE;
+    return markov_draft_impl(U, W1, W2, wdtype, w2_layout, anchor, H, B, K, V, r, mode, seed, temperature, tokens,
+                             logprobs, ws, kScratchBytes, stream, nullptr, nullptr);
 }
 
 int dspark_markov_status(const void* workspace, size_t workspace_bytes, int B, int K, void* stream) {
