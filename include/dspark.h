@@ -152,6 +152,16 @@ int dspark_markov_draft_noalloc(const float* U, const void* W1, const void* W2, 
 int dspark_markov_status(const void* workspace, size_t workspace_bytes, int B, int K, void* stream);
 
 /*
+ * Launch of the whole-round kernel, for the calls that follow in this process.  The kernel runs one workgroup
+ * per CU and synchronises them at every position, so all must be resident together.  By default (on = 0) it is
+ * an ordinary launch: on a device that runs nothing else at the same time every workgroup is resident at once.
+ * The runtime's cooperative launch (on = 1) guarantees co-residency even on a shared device, at a cost of
+ * about 20 us per call on MI355X.  With the ordinary launch on a device shared with kernels that hold CUs for
+ * long, the round's bounded waits can give up: the kernel still exits, and dspark_markov_status reports it.
+ */
+void dspark_set_cooperative_launch(int on);
+
+/*
  * Testing hook: the number of sleeps after which a bounded wait of the whole-round kernel gives up, for the
  * calls that follow in this process (0 restores the default, 2^22).  A tiny limit forces the failure path of
  * dspark_markov_status without faulting: every wait still ends and the kernel exits normally.

@@ -52,6 +52,7 @@ def _load_lib():
         "dspark_markov_draft_noalloc": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp],
                                         i32),
         "dspark_set_spin_limit": ([ctypes.c_uint32], None),
+        "dspark_set_cooperative_launch": ([i32], None),
         "dspark_markov_draft_confidence": ([vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, i32, vp,
                                             vp, vp, vp, vp, vp, sz, vp], i32),
         "dspark_markov_step": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, u64, f32, vp, vp, vp, vp, sz,
@@ -211,6 +212,11 @@ def dspark_markov_status(workspace, B, K, *, stream=None):
     with _on(stream):
         return int(_lib.dspark_markov_status(_p(workspace), workspace.numel() * workspace.element_size(), B, K,
                                              _stream(stream)))
+
+
+def dspark_set_cooperative_launch(on: bool):
+    """Whole-round kernel launch for later calls: ordinary (default) or cooperative (guaranteed co-residency)."""
+    _lib.dspark_set_cooperative_launch(1 if on else 0)
 
 
 def dspark_set_spin_limit(sleeps: int):

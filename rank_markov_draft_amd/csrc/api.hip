@@ -30,6 +30,7 @@ int device_fail(hipError_t e, const char* what) {
 constexpr int kMaxG = 1024;          // upper bound on workgroups along the vocabulary
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // sleeps before a bounded wait of the round kernel gives up
 std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+std::atomic<int> g_cooperative{0};  // whole-round kernel: ordinary launch (0) or cooperative launch (1)
 constexpr int kRowPad = 128;         // partials are padded to whole 128-row blocks
 constexpr int kMfmaWGPerCU = 2;
 
@@ -259,7 +260,8 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
 
     // whole round in one persistent launch when the shape allows it
     const bool round_ok = mfma_eligible(wdtype, r) && round_supported_r(r) && layout == DSPARK_W2_VR && aligned16(W1) && aligned16(W2use) &&
-                          aligned16(U) && V % 4 == 0 && (!H || aligned16(H)) && coop_supported();
+                          aligned16(U) && V % 4 == 0 && (!H || aligned16(H)) &&
+                          (!g_cooperative.load(std::memory_order_relaxed) || coop_supported());
     if (round_ok) {
         const int ntiles = (V + 31) / 32;
         int G = round_max_coresident(r, sample, H != nullptr, round_small_block(B), logits_out != nullptr);
@@ -301,7 +303,8 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.p_idx = ws.p_idx;
             a.p_l = ws.p_l;
             a.logits_out = logits_out;
-            hipError_t e = launch_markov_round(a, sample, H != nullptr, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+            hipError_t e = launch_markov_round(a, sample, H != nullptr, g_cooperative.load(std::memory_order_relaxed) != 0,
+                                               st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
             if (e != hipSuccess) return device_fail(e, "draft round launch");
             if (kernel_launches) *kernel_launches = 1;
             return DSPARK_OK;
@@ -452,6 +455,8 @@ int dspark_markov_status(const void* workspace, size_t workspace_bytes, int B, i
     if (err) return fail(DSPARK_EDEVICE, "a bounded wait of the whole-round kernel gave up: tokens -1 / NaN where it failed");
     return DSPARK_OK;
 }
+
+void dspark_set_cooperative_launch(int on) { g_cooperative.store(on ? 1 : 0, std::memory_order_relaxed); }
 
 void dspark_set_spin_limit(uint32_t sleeps) { g_spin_limit.store(sleeps ? sleeps : kDefaultSpinLimit, std::memory_order_relaxed); }
 

@@ -122,8 +122,8 @@ int round_supported_r(int r);
 // A batch of at most 8 rows takes the round kernel's small-block form (one U unit per item, deeper stream).
 inline bool round_small_block(int B) { return B <= 8; }
 int round_max_coresident(int r, bool sample, bool gated, bool small, bool store = false);
-hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
-                               hipEvent_t ev_end);
+hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool cooperative, hipStream_t st,
+                               hipEvent_t ev_begin, hipEvent_t ev_end);
 
 int mfma_supported_r(int r);
 hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);

@@ -1021,14 +1021,21 @@ int round_max_coresident(int r, bool sample, bool gated, bool small, bool store)
     return per_cu * device_cu_count();
 }
 
-hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, hipStream_t st, hipEvent_t ev_begin,
-                               hipEvent_t ev_end) {
+// The grid is one workgroup per CU (at most the device's co-resident count), so on a device that runs nothing
+// else all workgroups are resident together and the grid barrier completes.  An ordinary launch is the default:
+// on this part the runtime's cooperative launch, which guarantees co-residency, adds about 20 us per call
+// (measured on the serving round, 0.452 against 0.474 ms).  A device shared with kernels that hold CUs for
+// long can keep workgroups waiting; the kernel's bounded waits then give up, it exits normally and reports the
+// failure in the error word (tokens -1).  `cooperative` selects the guaranteed launch instead.
+hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool cooperative, hipStream_t st,
+                               hipEvent_t ev_begin, hipEvent_t ev_end) {
     const void* fn = round_fn_r(a.r, sample, gated, round_small_block(a.B), a.logits_out != nullptr);
     if (!fn) return hipErrorInvalidValue;
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
     RoundArgs copy = a;
     void* args[] = {&copy};
-    const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st);
+    const hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st)
+                                     : hipLaunchKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st);
     if (ev_end) (void)hipEventRecord(ev_end, st);
     return e;
 }

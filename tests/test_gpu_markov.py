@@ -281,6 +281,20 @@ def test_full_batch1_greedy(D):
     _full_draft_check(D, w, None, S.GREEDY, 0, what="batch-1 greedy")
 
 
+def test_cooperative_launch_matches_default(D):
+    """The whole-round kernel launched cooperatively (guaranteed co-residency) drafts bit for bit what the
+    default ordinary launch drafts."""
+    w = S.strong("serving", B=128, K=3, V=4096, r=256, mode=S.SAMPLE)
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    a = D.dspark_markov_draft(*args, mode=D.DSPARK_SAMPLE, seed=4)
+    D.dspark_set_cooperative_launch(True)
+    try:
+        b = D.dspark_markov_draft(*args, mode=D.DSPARK_SAMPLE, seed=4)
+    finally:
+        D.dspark_set_cooperative_launch(False)
+    assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
+
+
 def test_device_timeout_is_reported(D):
     """Failure path of the whole-round kernel, forced from the host: a spin limit of one sleep makes its bounded
     waits give up (every wait still ends, so the kernel exits normally).  The status call then reports
