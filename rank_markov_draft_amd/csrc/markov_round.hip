@@ -438,11 +438,18 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 }
             }
         };
+        // The 16-byte LDS writes of an item go out in pairs with a short sleep between pairs.  Eight writes in a
+        // burst (32 KB per CU per item over the four producers) delay the consumer waves' operand reads on the
+        // same CU: a consumer's tile took 0.74 us with the producers writing and 0.42 us without.  The producers
+        // mostly wait for a free stage anyway, so spacing the writes costs them nothing (serving round 0.463 ->
+        // 0.453 ms mean, with a much shorter tail, in same-box A/B; wider spacing starts to delay the stream).
         auto store = [&](int i, const u32x4_t (&src)[NU]) {
             uint8_t* st = ring + (i % RG::kNS) * RG::kStage;
 #pragma unroll
-            for (int n = 0; n < NU; ++n)
+            for (int n = 0; n < NU; ++n) {
                 if (p + 4 * n < RG::kUnits) *reinterpret_cast<u32x4_t*>(st + soff[n]) = src[n];
+                if (UR == 16 && n % 2 == 1 && n + 1 < NU) __builtin_amdgcn_s_sleep(3);
+            }
         };
         auto publish = [&](int i, const u32x4_t (&src)[NU]) {
             if (i >= RG::kNS) {
