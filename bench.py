@@ -18,11 +18,14 @@ reads; that variant is reported as an extra.)  The printed line is one JSON obje
                    W2 + U_k + gathered W1 rows + predecessors + outputs) over the kernel's mean duration,
                    timed with HIP events on the library's stream around each launch; traffic = the
                    counter-measured bytes per launch recorded for the current kernel source
-    cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload, on this host's cores
-    extras         the back-to-back (no eviction), write-fill and graph-replay rates, the practical streaming
-                   ceiling of the round's bytes (read_ceiling), and the other measured shapes (greedy,
-                   confidence head, prefix scheduler, top-16 Selector and its top-k sweep, gated head,
-                   batch 1)
+    cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload, on this host's cores (model,
+                   sockets and SMT stated), run along the GPU's drafted tokens so that the same run gives the
+                   parity counts of the measured round (flagged positions, differing tokens); plus one
+                   single-thread batch-1 round
+    extras         the back-to-back (no eviction), write-fill, graph-replay and cooperative-launch rates, the
+                   practical streaming ceiling of the round's bytes (read_ceiling), and the other measured shapes
+                   (greedy, confidence head, prefix scheduler, top-16 Selector and its top-k sweep on three input
+                   recipes, gated head and its top-16 Selector form, batch 1, the tiny workload's latency)
 """
 import argparse
 import hashlib
@@ -97,6 +100,28 @@ def write_traffic(fetch_csv, write_csv):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+def host_cpu():
+    """Model, sockets, threads per core and the CPUs this process may use."""
+    model, sockets, threads_per_core = None, None, None
+    try:
+        ids = set()
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name") and model is None:
+                model = line.split(":", 1)[1].strip()
+            if line.startswith("physical id"):
+                ids.add(line.split(":", 1)[1].strip())
+        sockets = len(ids) or None
+    except OSError:
+        pass
+    try:
+        smt = open("/sys/devices/system/cpu/smt/active").read().strip()
+        threads_per_core = 2 if smt == "1" else 1
+    except OSError:
+        pass
+    return {"model": model, "sockets": sockets, "smt_threads_per_core": threads_per_core,
+            "usable_cpus": len(os.sched_getaffinity(0)), "logical_cpus": os.cpu_count()}
 
 
 def main():
@@ -185,6 +210,7 @@ def main():
     torch.cuda.synchronize()
     ms, wall = timed_rounds(serving_round, args.steps)
     ms_per_step = float(ms.mean())
+    serving_tokens = tokens.cpu().numpy()  # the drafted tokens, for the CPU leg's parity counts
     value = B * K / (ms_per_step / 1e3)
     bytes_pos = markov_bytes_per_position(B, V, r)
     roof_round_ms = K * bytes_pos / (HBM_PEAK_GBS * 1e9) * 1e3
@@ -236,6 +262,7 @@ def main():
         serving_round()
     torch.cuda.synchronize()
     ms_graph, _ = timed_rounds(graph.replay, args.steps)
+    del graph
 
     # the same round with the runtime's cooperative launch (guaranteed co-residency) instead of the default
     D.dspark_set_cooperative_launch(True)
@@ -350,16 +377,22 @@ def main():
                                     "pct_of_hbm_roofline": round(100.0 * sb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(sms_.mean()), 2)}
 
         # top-k sweep: the Selector execution of the Markov rule (W1 = A, W2 = Bemb^T) restricted to the
-        # top-k candidates, against the full-vocabulary greedy head on the same inputs: token agreement and
-        # round time, on these inputs and on a strong-bias variant of them
+        # top-k candidates, against the full-vocabulary greedy head on the same inputs: token agreement (and the
+        # longest agreeing prefix) for three recipes, and the round time (the same bytes for every recipe).  The
+        # serving recipe's bias (std 0.006) is far below its hot-token boost, so there the truncation never binds;
+        # the moderate (bias std 0.3) and strong (1.0) recipes use U = z + 2 on the hot ids.
         sweep = {}
-        for label, wk in (("synthetic", w), ("strong_bias", S.strong("selector"))):
-            if label != "synthetic":
-                del U, A, Bemb
-                torch.cuda.empty_cache()
-                U = torch.from_numpy(wk.U).to(dev)
-                A, Bemb = to_w(wk.W1), to_w(wk.W2T)
-                anc = torch.from_numpy(wk.anchor).to(dev)
+        for label in ("serving_recipe", "moderate_bias", "strong_bias"):
+            del U, A, Bemb
+            torch.cuda.empty_cache()
+            if label == "serving_recipe":
+                wk = S.workload("selector")
+            else:
+                bias_sd = 0.3 if label == "moderate_bias" else 1.0
+                wk = S.workload("selector", sigma_w=float(np.sqrt(bias_sd / np.sqrt(256))), u_scale=1.0, u_boost=2.0)
+            U = torch.from_numpy(wk.U).to(dev)
+            A, Bemb = to_w(wk.W1), to_w(wk.W2T)
+            anc = torch.from_numpy(wk.anchor).to(dev)
             full, _ = D.dspark_markov_draft(U, A, Bemb, anc, w2_layout=D.DSPARK_W2_VR, mode=D.DSPARK_GREEDY)
             fh = full.cpu().numpy()
             row = {}
@@ -371,7 +404,7 @@ def main():
                 same = th == fh
                 prefix = np.where(same.all(axis=1), wk.K, np.argmin(same, axis=1))
                 ent = {"agreement": round(float(same.mean()), 4), "mean_agreeing_prefix": round(float(prefix.mean()), 3)}
-                if label == "synthetic":
+                if label == "serving_recipe":
                     kms, _ = timed_rounds(lambda: D.dspark_selector_draft(U, A, Bemb, anc, topk=kk, workspace=kws), 5)
                     ent["round_ms"] = round(float(kms.mean()), 4)
                 row["k%d" % kk] = ent
@@ -401,6 +434,22 @@ def main():
         extras["gated"] = {"round_ms": round(float(gms_.mean()), 4),
                            "tokens_per_s": round(w.B * w.K / (gms_.mean() / 1e3), 1), "bytes_per_round": gb,
                            "pct_of_hbm_roofline": round(100.0 * gb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gms_.mean()), 2)}
+
+        # its top-16 Selector form: the gate GEMM, then top-16, the gated pair tables and the walk
+        gsws = torch.empty(D.dspark_selector_workspace_bytes(w.B, w.K, w.V, w.r, 16), dtype=torch.uint8, device=dev)
+
+        def gated_sel_round():
+            D.dspark_gate(h, Wg, out=Hbuf)
+            D.dspark_selector_draft(U, W1g, W2g, anc, H=Hbuf, topk=16, workspace=gsws)
+
+        gated_sel_round()
+        gsms, _ = timed_rounds(gated_sel_round, 10)
+        gsb = (selector_bytes_per_round(w.B, w.K, w.V, w.r) + 2 * w.B * w.K * w.D + 2 * w.D * w.r
+               + 2 * 4 * w.B * w.K * w.r)
+        extras["gated_selector_top16"] = {
+            "round_ms": round(float(gsms.mean()), 4), "tokens_per_s": round(w.B * w.K / (gsms.mean() / 1e3), 1),
+            "bytes_per_round": gsb,
+            "pct_of_hbm_roofline": round(100.0 * gsb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gsms.mean()), 2)}
         del U, W1g, W2g, h, Wg
         torch.cuda.empty_cache()
 
@@ -425,6 +474,27 @@ def main():
         del U, W1b, W2b
         torch.cuda.empty_cache()
 
+        # the tiny workload (B=1, K=4, V=512, r=16, fp32 weights, greedy): launch-bound latency of one draft, of
+        # the full head and of its top-k = V Selector form (no eviction: the operands are 74 KB)
+        w = S.workload("tiny")
+        U = torch.from_numpy(w.U).to(dev)
+        W1t, W2t = torch.from_numpy(w.W1).to(dev), torch.from_numpy(w.W2).to(dev)
+        W2tT = torch.from_numpy(np.ascontiguousarray(w.W2.T)).to(dev)
+        anc = torch.from_numpy(w.anchor).to(dev)
+        tws = torch.empty(D.dspark_markov_workspace_bytes(1, w.K, w.V, w.r, 0, 0), dtype=torch.uint8, device=dev)
+        sws_t = torch.empty(D.dspark_selector_workspace_bytes(1, w.K, w.V, w.r, w.V), dtype=torch.uint8, device=dev)
+        tiny_head = lambda: D.dspark_markov_draft(U, W1t, W2t, anc, w2_layout=D.DSPARK_W2_RV, workspace=tws)
+        tiny_sel = lambda: D.dspark_selector_draft(U, W1t, W2tT, anc, topk=w.V, workspace=sws_t)
+        tiny_head(), tiny_sel()
+        tms, _ = timed_rounds(tiny_head, 20, flush=False)
+        tsms, _ = timed_rounds(tiny_sel, 20, flush=False)
+        extras["tiny_latency"] = {"workload": "B=1, K=4, V=512, r=16, fp32, greedy",
+                                  "markov_draft_us": round(1e3 * float(tms.mean()), 1),
+                                  "selector_topk_V_us": round(1e3 * float(tsms.mean()), 1),
+                                  "kernel_launches": {"markov_draft": 2 * w.K, "selector": 3}}
+        del U
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu:
@@ -440,12 +510,30 @@ def main():
         nrows = max(threads, nrows) if nrows < w.B else w.B
         nrows = min(nrows, w.B)
         rows = list(range(nrows))
+        # the oracle runs along the GPU's drafted tokens (teacher forcing), so the same timed run also gives the
+        # parity counts of the measured round on these rows
         t0 = time.perf_counter()
-        O.markov_draft(w.U, w.W1, W2Th, w.anchor, w2_layout=O.W2_VR, mode=O.SAMPLE, seed=w.noise_seed, rows=rows)
+        ref = O.markov_draft(w.U, w.W1, W2Th, w.anchor, w2_layout=O.W2_VR, mode=O.SAMPLE, seed=w.noise_seed,
+                             follow=serving_tokens, rows=rows)
         dt = time.perf_counter() - t0
+        agree = serving_tokens[rows] == ref["tokens"][rows]
+        parity = {"rows": nrows, "positions": int(agree.size),
+                  "flagged_margin_below_2e-2": int((ref["margins"][rows] < 2e-2).sum()),
+                  "tokens_differing": int((~agree).sum()),
+                  "differing_and_unreachable": int((~agree & (ref["reach"][rows] != 1)).sum())}
+        # one single-thread batch-1 round (per-core scale)
+        wb = S.workload("batch1")
+        O.set_num_threads(1)
+        t1 = time.perf_counter()
+        O.markov_draft(wb.U, wb.W1, wb.W2T, wb.anchor, w2_layout=O.W2_VR)
+        dt1 = time.perf_counter() - t1
+        O.set_num_threads(threads)
         cpu = {"value": round(nrows * w.K / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"serving workload rows 0..{nrows - 1} of {w.B}, all {w.K} positions, sampling T=1 "
-                         f"({nrows * w.K} draft tokens, fp64, {dt:.1f} s)"}
+                         f"({nrows * w.K} draft tokens, fp64, {dt:.1f} s)",
+               "host": host_cpu(), "parity_of_measured_round": parity,
+               "batch1_single_thread": {"tokens_per_s": round(wb.K / dt1, 3), "round_s": round(dt1, 2),
+                                        "workload": "B=1, K=16, V=151936, r=256, greedy, one thread"}}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -457,6 +545,11 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extras": extras,
     }
     print(json.dumps(out), flush=True)
+    # orderly teardown: wait for the device, then release torch's cached blocks while the runtime is up
+    torch.cuda.synchronize()
+    del flush_buf, ws, tokens, logprobs, W1, W2T
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

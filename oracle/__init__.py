@@ -33,6 +33,7 @@ def _load():
                                        ctypes.c_double, ctypes.c_void_p)
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
         lib.oracle_fmix32.argtypes = [u32]
         lib.oracle_fmix32.restype = u32
         lib.oracle_noise_bits.argtypes = [u64, u32, u32, u32]
@@ -90,6 +91,11 @@ def _rows(rows: Optional[Sequence[int]]):
 def num_threads() -> int:
     """Threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int):
+    """Threads for the oracle's later parallel loops."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------------------------- noise

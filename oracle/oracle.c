@@ -86,8 +86,9 @@ static uint32_t murmur3_fmix32(uint32_t h) {
 
 uint32_t oracle_fmix32(uint32_t h) { return murmur3_fmix32(h); }
 
-/* Threads the parallel loops below use (OpenMP's current maximum). */
+/* Threads the parallel loops below use (OpenMP's current maximum), and a setter (n >= 1). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* Chained key: k0 from the 64-bit seed, then the row, the position and the vocabulary id are
  * folded in one at a time, each followed by a full finalisation mix. */

@@ -104,7 +104,7 @@ __device__ __forceinline__ float wave_lth_largest(float t) {
     return __shfl(t, 64 - L);
 }
 
-// Top-k (k <= L, L = 16 or 64) of each row, one workgroup per row.  Each wave keeps an exact top-L list (one
+// Top-k (k <= L, L = 16, 32 or 64) of each row, one workgroup per row.  Each wave keeps an exact top-L list (one
 // entry per lane 0..L-1) and its L-th entry as a threshold; every element is compared once against the
 // threshold and the few that beat it are appended to the wave's LDS buffer, which is merged into the list
 // when it fills.  The row is streamed with kTkUnroll independent 16-byte loads per lane, so the scan runs at
@@ -116,6 +116,8 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
     __shared__ int bufi[kTkWaves][kTkBuf];
     __shared__ float finv[kTkWaves * L];
     __shared__ int fini[kTkWaves * L];
+    __shared__ float sthv[kTkWaves];  // each wave's current threshold (its list entry L-1): any of them is a
+    __shared__ int sthi[kTkWaves];    // bound for the whole row, so every wave filters with the best of them
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x;
@@ -125,11 +127,38 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
     float tv = -INFINITY, thv = -INFINITY;  // this lane's list entry; the wave's threshold (list entry L-1)
     int ti = 0x7FFFFFFF, thi = 0x7FFFFFFF;
     int cnt = 0;                            // wave-uniform buffer fill
+    if (lane == 0) {
+        sthv[wave] = -INFINITY;
+        sthi[wave] = 0x7FFFFFFF;
+    }
+    __syncthreads();
 
+    // An element behind (after, in the order) the L-th entry of any wave's list has L elements of the row ahead
+    // of it, so it is not in the row's top L: the waves share their thresholds and filter with the best one.
+    auto adopt_shared = [&]() {
+#pragma unroll
+        for (int w = 0; w < kTkWaves; ++w) {
+            const float ov = sthv[w];
+            const int oi = sthi[w];
+            if (before(ov, oi, thv, thi)) {
+                thv = ov;
+                thi = oi;
+            }
+        }
+    };
     auto flush = [&]() {
         wave_top_merge<L>(bv, bi, cnt, tv, ti);
-        thv = __shfl(tv, L - 1);
-        thi = __shfl(ti, L - 1);
+        const float nv = __shfl(tv, L - 1);
+        const int ni = __shfl(ti, L - 1);
+        if (lane == 0) {
+            sthv[wave] = nv;
+            sthi[wave] = ni;
+        }
+        if (before(nv, ni, thv, thi)) {
+            thv = nv;
+            thi = ni;
+        }
+        if (L > 16) adopt_shared();
         cnt = 0;
     };
     auto offer = [&](float x, int id) {
@@ -173,6 +202,8 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
                 // of the first chunk is a candidate and the merges of the start dominate the scan.
                 thv = wave_lth_largest<L>(mx);
                 thi = 0x7FFFFFFF;
+            } else if (L > 16 && (q0 / (kTkThreads * kTkUnroll)) % 4 == 0) {
+                adopt_shared();  // pick up the other waves' progress now and then
             }
             if (__ballot(mx >= thv)) {
 #pragma unroll
@@ -693,6 +724,9 @@ hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int to
     if (topk <= 16) {
         if (vec) hipLaunchKernelGGL((topk_kernel<16, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
         else hipLaunchKernelGGL((topk_kernel<16, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+    } else if (topk <= 32) {
+        if (vec) hipLaunchKernelGGL((topk_kernel<32, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
+        else hipLaunchKernelGGL((topk_kernel<32, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
     } else if (topk <= 64) {
         if (vec) hipLaunchKernelGGL((topk_kernel<64, true>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
         else hipLaunchKernelGGL((topk_kernel<64, false>), dim3(rows), dim3(kTkThreads), 0, st, U, u_stride, V, topk, idx, val);
