@@ -273,8 +273,9 @@ size_t dspark_topk_workspace_bytes(int rows, int V, int topk);
  * equal.  (Equivalence page, section "Where the parallelism comes from": the candidate set of a
  * position is the top tokens under the base logits.)
  * U [rows, V] fp32 with row i at U + i * u_stride.  idx [rows, topk] int32 output, val [rows, topk]
- * fp32 output or NULL.  1 <= topk <= V; topk <= 64 at any V (DSPARK_EUNSUPPORTED for topk > 64 unless
- * V <= 4096, where the row is sorted whole).
+ * fp32 output or NULL.  1 <= topk <= V; topk <= 1024 at any V (DSPARK_EUNSUPPORTED for topk > 1024
+ * unless V <= 4096, where the row is sorted whole).  topk <= 64 takes one pass over the row; 64 < topk <=
+ * 1024 at V > 4096 takes a radix selection that reads the row four times.
  */
 int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int32_t* idx, float* val,
                 void* workspace, size_t workspace_bytes, void* stream);

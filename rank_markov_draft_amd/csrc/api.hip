@@ -615,7 +615,7 @@ int dspark_topk(const float* U, int64_t u_stride, int rows, int V, int topk, int
     if (rows <= 0 || V <= 0) return fail(DSPARK_EINVAL, "rows and V must be positive");
     if (u_stride < V) return fail(DSPARK_EINVAL, "u_stride < V");
     if (topk < 1 || topk > V) return fail(DSPARK_EINVAL, "topk %d outside [1, V]", topk);
-    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 64 needs V <= 4096");
+    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 1024 needs V <= 4096");
     hipError_t e = launch_topk(U, u_stride, rows, V, topk, idx, val, nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return device_fail(e, "topk launch");
     return DSPARK_OK;
@@ -649,7 +649,7 @@ int dspark_selector_draft(const float* U, const void* A, const void* Bemb, int w
     if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE) return fail(DSPARK_EINVAL, "unknown mode %d", mode);
     if (mode == DSPARK_SAMPLE && !(temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0 when sampling");
     if (topk < 1 || topk > V) return fail(DSPARK_EINVAL, "topk %d outside [1, V]", topk);
-    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 64 needs V <= 4096");
+    if (!topk_supported(V, topk)) return fail(DSPARK_EUNSUPPORTED, "topk > 1024 needs V <= 4096");
     if (topk > 1024) return fail(DSPARK_EUNSUPPORTED, "the walk takes at most 1024 candidates (topk = %d)", topk);
     if (r > 1024) return fail(DSPARK_EUNSUPPORTED, "r = %d exceeds 1024", r);
     if ((size_t)B * K > 2147483647u) return fail(DSPARK_EUNSUPPORTED, "B * K too large");

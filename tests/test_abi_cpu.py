@@ -119,7 +119,7 @@ def test_selector_gate_topk_argument_errors(lib):
     s = lib.dspark_selector_draft
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 0, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 1
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 101, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 1
-    assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 8192, 16, 65, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 2
+    assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 8192, 16, 1025, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 2
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 16, 0, 0, 1.0, FAKE, None, None, None, FAKE, 8, None) == 3
     g = lib.dspark_gate
     assert g(None, FAKE, 4, 256, 32, FAKE, None) == 1
@@ -128,7 +128,7 @@ def test_selector_gate_topk_argument_errors(lib):
     t = lib.dspark_topk
     assert t(FAKE, 100, 4, 100, 0, FAKE, None, None, 0, None) == 1
     assert t(FAKE, 50, 4, 100, 4, FAKE, None, None, 0, None) == 1
-    assert t(FAKE, 8192, 4, 8192, 65, FAKE, None, None, 0, None) == 2
+    assert t(FAKE, 8192, 4, 8192, 1025, FAKE, None, None, 0, None) == 2
     p = lib.dspark_pack_w2
     assert p(None, 10, 10, 1, FAKE, None) == 1
     assert p(FAKE, 10, 10, 9, FAKE, None) == 1

@@ -48,6 +48,22 @@ def test_topk_large_k_small_vocab(D, V, k):
     assert np.array_equal(host(val), rval)
 
 
+@pytest.mark.parametrize("V,k", [(4097, 65), (5000, 100), (10007, 1024), (151936, 65), (151936, 256),
+                                 (151936, 1024), (129280, 700)], ids=lambda c: str(c))
+def test_topk_radix_select(D, V, k):
+    """64 < k <= 1024 at V > 4096: radix selection.  Rows with heavy ties, an all-equal row (the k lowest ids),
+    +-0 and a row of repeated maxima exercise the count of the k-th key's equals; large V uses logits rows."""
+    rows = 6 if V > 10000 else 8
+    U = _tie_rows(rows, V, seed=V + k) if V <= 10000 else S.logits(0xD5A10005, (rows,), V, 16)
+    if V > 10000:
+        U[1, ::3] = U[1].max()  # many equal maxima: the top-k is the lowest ids among them
+        U[2] = -0.0
+    idx, val = D.dspark_topk(t_f32(U), k)
+    ridx, rval = O.topk(U, k)
+    assert np.array_equal(host(idx), ridx)
+    assert np.array_equal(host(val), rval)
+
+
 SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 96, 16, 16, S.F32),
               (130, 2, 513, 48, 16, S.BF16), (2, 3, 300, 520, 16, S.BF16), (3, 3, 2000, 32, 32, S.BF16),
               (2, 3, 5000, 64, 64, S.BF16),
@@ -55,7 +71,9 @@ SEL_SHAPES = [(3, 4, 200, 32, 16, S.BF16), (5, 3, 1000, 64, 5, S.BF16), (2, 5, 9
               (4, 4, 3000, 256, 16, S.BF16),
               # K = 16 with k = 32 (the row-parallel walk with more than 64 KB of LDS) and k = 64 (tables
               # beyond the workgroup's LDS, walked step by step from global memory)
-              (2, 16, 1000, 32, 32, S.BF16), (2, 16, 1000, 32, 64, S.BF16)]
+              (2, 16, 1000, 32, 32, S.BF16), (2, 16, 1000, 32, 64, S.BF16),
+              # k > 64 at V > 4096 (radix-selected candidates)
+              (2, 3, 5000, 32, 100, S.BF16), (2, 3, 5000, 16, 1024, S.BF16)]
 
 
 def _restricted_check(D, w, A, Bemb, H, cand, tok, lp, mode, seed, T, what, rows=None):
