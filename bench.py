@@ -258,41 +258,45 @@ def main():
         torch.cuda.synchronize()
         ms_dirty.append(e0.elapsed_time(e1))
 
-    # the same round captured once in a graph and replayed (evicted like the plain enqueue)
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.graph(graph, stream=side):
+    # The same round captured once in a graph and replayed, the same round with the runtime's cooperative launch,
+    # and the streaming ceiling: extras (a counter or trace run with --no-extras launches only the plain rounds).
+    ms_graph = ms_coop = rd_ms = None
+    read_bytes = 0
+    if not args.no_extras:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=side):
+            serving_round()
+        torch.cuda.synchronize()
+        ms_graph, _ = timed_rounds(graph.replay, args.steps)
+        del graph
+
+        # the cooperative launch guarantees co-residency; the default ordinary launch relies on one workgroup per CU
+        D.dspark_set_cooperative_launch(True)
         serving_round()
-    torch.cuda.synchronize()
-    ms_graph, _ = timed_rounds(graph.replay, args.steps)
-    del graph
+        ms_coop, _ = timed_rounds(serving_round, max(3, min(args.steps, 10)))
+        D.dspark_set_cooperative_launch(False)
 
-    # the same round with the runtime's cooperative launch (guaranteed co-residency) instead of the default
-    D.dspark_set_cooperative_launch(True)
-    serving_round()
-    ms_coop, _ = timed_rounds(serving_round, max(3, min(args.steps, 10)))
-    D.dspark_set_cooperative_launch(False)
+        # Practical streaming ceiling: the round's operand bytes (W2 and each position's base logits, here as 16
+        # contiguous regions of U) read once per position by a plain streaming kernel, 16 launches replayed from
+        # a HIP graph after the same eviction.  Reported beside the nominal peak; the round is not held to it.
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        u_flat = U.view(-1)
+        per_pos = B * V
 
-    # Practical streaming ceiling: the round's operand bytes (W2 and each position's base logits, here as 16
-    # contiguous regions of U) read once per position by a plain streaming kernel, 16 launches replayed from a
-    # HIP graph after the same eviction.  Reported beside the nominal peak; the round is not held to it.
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    u_flat = U.view(-1)
-    per_pos = B * V
+        def read_round():
+            for k in range(K):
+                D.dspark_stream_read(W2T, u_flat[k * per_pos:(k + 1) * per_pos], sink)
 
-    def read_round():
-        for k in range(K):
-            D.dspark_stream_read(W2T, u_flat[k * per_pos:(k + 1) * per_pos], sink)
-
-    read_round()
-    torch.cuda.synchronize()
-    read_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(read_graph):
         read_round()
-    rd_ms, _ = timed_rounds(read_graph.replay, max(3, min(args.steps, 10)))
-    read_bytes = K * (W2T.numel() * W2T.element_size() + per_pos * 4)
-    del read_graph
+        torch.cuda.synchronize()
+        read_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(read_graph):
+            read_round()
+        rd_ms, _ = timed_rounds(read_graph.replay, max(3, min(args.steps, 10)))
+        read_bytes = K * (W2T.numel() * W2T.element_size() + per_pos * 4)
+        del read_graph
 
     extras = {
         "round_ms_p10": round(float(np.percentile(ms, 10)), 4), "round_ms_p90": round(float(np.percentile(ms, 90)), 4),
@@ -302,16 +306,19 @@ def main():
         "back_to_back_round_ms": round(float(ms_b2b.mean()), 4),
         "back_to_back_tokens_per_s": round(B * K / (float(ms_b2b.mean()) / 1e3), 1),
         "after_write_fill_round_ms": round(float(np.mean(ms_dirty)), 4),
-        "graph_replay_round_ms": round(float(ms_graph.mean()), 4),
-        "cooperative_launch_round_ms": round(float(ms_coop.mean()), 4),
-        "graph_replay_tokens_per_s": round(B * K / (float(ms_graph.mean()) / 1e3), 1),
         "timed_wall_s": round(wall, 4),
-        "read_ceiling": {"what": "the round's W2 and base-logit bytes read once per position by a plain streaming "
-                                 "kernel (dspark_stream_read, 16 launches from a HIP graph), evicted like a round",
-                         "round_ms": round(float(rd_ms.mean()), 4), "bytes": int(read_bytes),
-                         "GB_per_s": round(read_bytes / (float(rd_ms.mean()) / 1e3) / 1e9, 1),
-                         "serving_round_fraction": round(float(rd_ms.mean()) / ms_per_step, 4)},
     }
+    if ms_graph is not None:
+        extras.update({
+            "graph_replay_round_ms": round(float(ms_graph.mean()), 4),
+            "graph_replay_tokens_per_s": round(B * K / (float(ms_graph.mean()) / 1e3), 1),
+            "cooperative_launch_round_ms": round(float(ms_coop.mean()), 4),
+            "read_ceiling": {"what": "the round's W2 and base-logit bytes read once per position by a plain "
+                                     "streaming kernel (dspark_stream_read, 16 launches from a HIP graph), evicted "
+                                     "like a round",
+                             "round_ms": round(float(rd_ms.mean()), 4), "bytes": int(read_bytes),
+                             "GB_per_s": round(read_bytes / (float(rd_ms.mean()) / 1e3) / 1e9, 1),
+                             "serving_round_fraction": round(float(rd_ms.mean()) / ms_per_step, 4)}})
     if not args.no_extras:
         # the same sampling round with the confidence head and prefix survival (synthetic hidden states, D = 4096,
         # as the gated workload's): computed by the round kernel's finalizer waves, one position behind

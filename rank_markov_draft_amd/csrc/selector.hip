@@ -1041,8 +1041,8 @@ hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
 
 hipError_t launch_walk(const SelectorArgs& a, hipStream_t st) {
     // Rows resolved in parallel, the padded tables staged in LDS whole when they fit (160 KB on this part: top-16
-    // and top-32 at K = 16), else in chunks (top-64 at K = 16); one step at a time from global memory only when
-    // even the per-row picks and per-step candidate data exceed the LDS.
+    // and top-32 at K = 16), else in chunks of at least a quarter of a workgroup's threads in rows (top-64 at
+    // K = 16); otherwise one step at a time from global memory.
     auto allow = [](const void* fn) {
         return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kWalkLdsMax) == hipSuccess
                    ? (size_t)kWalkLdsMax
@@ -1055,8 +1055,11 @@ hipError_t launch_walk(const SelectorArgs& a, hipStream_t st) {
         allow(reinterpret_cast<const void*>(&walk_rows_kernel<64>)));
     const size_t fixed = walk_rows_fixed_bytes(a.K, a.topk), per_row = walk_rows_row_bytes(a.topk);
     const size_t rows = 1 + (size_t)(a.K - 1) * a.topk;
-    if (fixed + per_row <= lds_cap) {
-        const size_t fit = (lds_cap - fixed) / per_row, chunk = rows < fit ? rows : fit;
+    // Chunks of fewer rows than the workgroup has threads would leave most of it idle for every chunk's staging
+    // and resolution (top-512 at K = 4 took 1.9 ms so, against 0.02 ms step by step).
+    const size_t fit = fixed + per_row <= lds_cap ? (lds_cap - fixed) / per_row : 0;
+    if (fit >= rows || fit >= (size_t)kWalkThreads / 4) {
+        const size_t chunk = rows < fit ? rows : fit;
         const size_t lds = fixed + chunk * per_row;
         const dim3 g(a.B), blk(kWalkThreads);
         switch (a.topk) {
