@@ -264,7 +264,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
                           (!g_cooperative.load(std::memory_order_relaxed) || coop_supported());
     if (round_ok) {
         const int ntiles = (V + 31) / 32;
-        int G = round_max_coresident(r, sample, H != nullptr, round_small_block(B), logits_out != nullptr);
+        int G = round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
         if (G > round_gmax()) G = round_gmax();
         if (G > ntiles) G = ntiles;
         if (G >= 1) {

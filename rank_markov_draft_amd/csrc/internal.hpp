@@ -119,9 +119,12 @@ constexpr int kWinnerSlots = 1;
 constexpr int kBarrierGroups = 8;
 constexpr int kCounterStride = 32;  // words between counters (128 bytes)
 int round_supported_r(int r);
-// A batch of at most 8 rows takes the round kernel's small-block form (one U unit per item, deeper stream).
-inline bool round_small_block(int B) { return B <= 8; }
-int round_max_coresident(int r, bool sample, bool gated, bool small, bool store = false);
+// Row forms of the round kernel: a batch of at most 8 rows takes the small-block form (one U unit per item,
+// deeper stream), 9 .. 64 rows the half-block form (eight U units per item, two sets of consumer waves), more
+// rows the full 128-row blocks.
+constexpr int kRowsFull = 0, kRowsHalf = 1, kRowsSmall = 2;
+inline int round_row_form(int B) { return B <= 8 ? kRowsSmall : B <= 64 ? kRowsHalf : kRowsFull; }
+int round_max_coresident(int r, bool sample, bool gated, int form, bool store = false);
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool cooperative, hipStream_t st,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 

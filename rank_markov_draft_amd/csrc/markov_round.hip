@@ -38,7 +38,9 @@
 //  * A batch of at most 8 rows takes a small-block form: one U unit per item instead of sixteen, so the
 //    producers keep six items in flight and the ring has eight stages (a stream of W2-only items is bound by
 //    the bytes in flight), and (without the gate) the four consumer waves each take every fourth tile of a
-//    position for the same rows, handing their per-row results to wave 0 through LDS.
+//    position for the same rows, handing their per-row results to wave 0 through LDS.  A batch of 9 .. 64
+//    rows takes a half-block form the same way: eight U units per item, five stages, and two sets of two
+//    consumer waves taking every other tile, so no consumer wave idles on rows past the batch.
 //  * The gated gather X = bf16(W1[a] (.) H) runs in four phases whose loads are all issued before their
 //    multiplies, so it costs the pick read and four memory round trips.
 #include <type_traits>
@@ -54,13 +56,16 @@ constexpr int kRTileV = 32;
 constexpr int kRRows = 128;
 constexpr float kNegBig = -1e30f;  // start of a running max; stays finite when scaled by log2(e)/T
 
-// UR = U units (8 rows each) per item: 16 for a full 128-row block; 1 for a batch of at most 8 rows, whose
+// UR = U units (8 rows each) per item: 16 for a full 128-row block; 8 for a batch of 9 .. 64 rows (a half
+// block: the LDS the missing U rows would take holds a fifth stage); 1 for a batch of at most 8 rows, whose
 // items are W2 almost only: then the registers and LDS that U rows would take hold more items instead (six in
 // flight per producer, eight stages), since a stream of small items is bound by the bytes in flight.
-template <int RK, int UR = 16>
+// HL: the gated half block, whose LDS also holds the next position's gate rows, keeps three stages and one more
+// item in flight per producer instead.
+template <int RK, int UR = 16, bool HL = false>
 struct Ring {
-    static_assert(UR == 16 || UR == 1, "full or small row block");
-    static constexpr int kNS = UR == 16 ? 4 : 8;
+    static_assert(UR == 16 || UR == 8 || UR == 1, "full, half or small row block");
+    static constexpr int kNS = HL ? 3 : UR == 16 ? 4 : UR == 8 ? 5 : 8;
     static constexpr int kW2Row = 32 * RK + 16;            // one W2 row (r = 16 RK bf16) + 16-byte pad
     static constexpr int kW2Bytes = kRTileV * kW2Row;      // 32 rows
     static constexpr int kURow = 4 * kRTileV + 16;          // one U row of the tile (32 floats) + 16-byte pad
@@ -69,7 +74,7 @@ struct Ring {
     // one item = RK W2 units (64 lanes x 16 B) + UR U units (8 rows x 128 B); producer p takes units p, p + 4, ...
     static constexpr int kUnits = RK + UR;
     static constexpr int kUnitsPerProducer = (kUnits + 3) / 4;
-    static constexpr int kDepth = UR == 16 ? 3 : 6;         // items in flight per producer, in registers
+    static constexpr int kDepth = HL ? 4 : UR == 1 ? 6 : 3;  // items in flight per producer, in registers
 };
 
 constexpr int kConsumers = 4;
@@ -231,21 +236,30 @@ __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) 
 // epilogue; the contraction and the pick are the same code.
 template <int RK, int MODE, bool GATED, int UR, bool STORE = false>
 __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArgs a) {
-    using RG = Ring<RK, UR>;
+    // The gated half block keeps the gate rows of the next position in LDS (filled by the finalizer wave while the
+    // current position streams), so the gather after a grid barrier waits on the W1 rows only.
+    constexpr bool HLDS = GATED && UR == 8;
+    constexpr int kHPitch = 16 * RK + 4;  // floats per gate row in LDS (16-byte shift per row: no bank conflicts)
+    using RG = Ring<RK, UR, HLDS>;
     constexpr bool SAMPLE = MODE == kModeSample;
     // Consumer sets: a small block (at most 8 rows) leaves three of the four consumer waves without rows, so
     // each wave instead forms a set of its own on the same 32 rows and takes every fourth tile of a position
     // (slots s, s + 4, ...), handing its per-row results to set 0 through LDS at the end of the position (the
-    // greedy maximum and the block race are both maxima over tiles, merged in set order).  The gate keeps one
-    // set: the gated gather holds more registers, and with the hand-over code the kernel would spill at three
-    // waves per SIMD.
-    constexpr int SETS = (UR == 1 && !GATED) ? 4 : 1;
+    // greedy maximum and the block race are both maxima over tiles, merged in set order).  A half block (9 ..
+    // 64 rows) runs two sets of two waves the same way, taking every other tile.  The gated small block keeps
+    // one set: its gather holds more registers, and with the hand-over code it would spill at three waves per
+    // SIMD.
+    constexpr int SETS = UR == 8 ? 2 : (UR == 1 && !GATED) ? 4 : 1;
     constexpr int kRowWaves = kConsumers / SETS;  // consumer waves of one set (32 rows each)
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kNS * RG::kStage];
     __shared__ uint32_t ready[RG::kNS];  // +1 per producer per filled stage
     __shared__ uint32_t freed[RG::kNS];  // +1 per consumer wave per consumed stage
     __shared__ uint32_t stepdone;        // +1 per consumer wave per finished position
     __shared__ uint32_t released;        // last position whose predecessors are known (set by consumer wave 0)
+    // HLDS: H[b, j, :] of rows b < 64 for one position j >= 1; hready = positions filled, hdone = consumer-wave
+    // gathers of positions >= 1 done (the buffer is refilled once all consumer waves have read it)
+    __shared__ __attribute__((aligned(16))) float hbuf[HLDS ? 64 * kHPitch : 4];
+    __shared__ uint32_t hready, hdone;
     // sets 1 .. SETS-1 hand their per-row results of a position to set 0 here (double-buffered by segment
     // parity): key, id (bits), logit of the pick, base-2 max and sum of the log-sum-exp
     constexpr int kHand = SETS > 1 ? SETS - 1 : 1;
@@ -279,6 +293,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     if (threadIdx.x == 0) {
         stepdone = 0u;
         released = 0u;
+        hready = 0u;
+        hdone = 0u;
     }
     // every wave reads the epoch before workgroup 0 can advance it (at the very end of the launch)
     const uint64_t tag = launch_tag(a, agent_load(a.epoch));
@@ -312,6 +328,40 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         // g, g + G, ...  Until the last position this runs while the rest of the workgroup streams and
         // computes, off the serial path.
         for (int k = 0; k < a.K; ++k) {
+            if constexpr (HLDS) {
+                if (k + 1 < a.K) {
+                    // the gate rows of position k + 1, once every consumer wave has gathered position k
+                    uint32_t hs = 0;
+                    while (lds_load(&hdone) < (uint32_t)(kConsumers * k)) {
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++hs > spin_limit) {
+                            agent_store(a.error, 1u);
+                            break;
+                        }
+                    }
+                    constexpr int kQ = 4 * RK;  // 16-byte pieces per row
+                    constexpr int kBatch = 16;
+                    const int n4 = min(a.B, 64) * kQ;
+                    for (int e0 = 0; e0 < n4; e0 += 64 * kBatch) {
+                        f32x4_t hv[kBatch];
+#pragma unroll
+                        for (int q = 0; q < kBatch; ++q) {
+                            const int e = e0 + 64 * q + lane;
+                            const int b = e / kQ, c4 = e % kQ;
+                            hv[q] = e < n4 ? *reinterpret_cast<const f32x4_t*>(a.H + ((size_t)b * a.K + k + 1) * (16 * RK) + 4 * c4)
+                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        }
+#pragma unroll
+                        for (int q = 0; q < kBatch; ++q) {
+                            const int e = e0 + 64 * q + lane;
+                            if (e < n4) *reinterpret_cast<f32x4_t*>(hbuf + (e / kQ) * kHPitch + 4 * (e % kQ)) = hv[q];
+                        }
+                    }
+                    wait_lgkmcnt0();
+                    __asm__ volatile("" ::: "memory");
+                    if (lane == 0) lds_add(&hready, 1u);
+                }
+            }
             bool timed_out = false;
             uint32_t spins = 0;
             if (k + 1 < a.K) {
@@ -735,7 +785,38 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 }
             }
             const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(a.W1 + (size_t)pv * r);
-            if constexpr (GATED) {
+            if (HLDS && k > 0) {
+                // W1 row chunks first (they need only the pick), then the gate row from LDS once it is there
+                u32x4_t raw[RK];
+#pragma unroll
+                for (int q = 0; q < RK; ++q) raw[q] = wrow[2 * q + half];
+                uint32_t hs = 0;
+                while (lds_load(&hready) < (uint32_t)k) {
+                    __builtin_amdgcn_s_sleep(0);
+                    if (++hs > spin_limit) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+                __asm__ volatile("" ::: "memory");  // gate reads stay after the wait
+                const float* hl = hbuf + (valid_b ? b : 0) * kHPitch + 8 * half;
+#pragma unroll
+                for (int q = 0; q < RK; ++q) {
+                    const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(hl + 16 * q);
+                    const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(hl + 16 * q + 4);
+                    const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                    const uint32_t w32[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+                    uint32_t o32[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = bf16_to_f32((uint16_t)(w32[e] & 0xFFFFu)) * hf[2 * e];
+                        const float hi = bf16_to_f32((uint16_t)(w32[e] >> 16)) * hf[2 * e + 1];
+                        o32[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                    }
+                    const u32x4_t o = valid_b ? u32x4_t{o32[0], o32[1], o32[2], o32[3]} : u32x4_t{0u, 0u, 0u, 0u};
+                    xf[q] = __builtin_bit_cast(bf16x8_t, o);
+                }
+            } else if constexpr (GATED) {
                 // X = bf16(W1[a] * H) in phases of kPh 16-value chunks.  Each phase issues all of its loads (W1
                 // row chunks, H chunks) before its multiplies, so the gather costs the pick read and one memory
                 // round trip per phase, rather than one per chunk; four phases fit the register budget at
@@ -777,6 +858,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 }
             }
             if (SAMPLE) k2 = noise_key2(a.k0, (uint32_t)b, (uint32_t)k);
+        }
+        if (HLDS && k > 0 && rb == 0) {
+            // this wave's reads of the gate rows are done: the finalizer may refill the buffer
+            wait_lgkmcnt0();
+            __asm__ volatile("" ::: "memory");
+            if (lane == 0) lds_add(&hdone, 1u);
         }
         if constexpr (STORE) store_row = valid_b ? a.logits_out + ((size_t)b * a.K + k) * (size_t)a.V : nullptr;
         m = kNegBig;
@@ -1000,29 +1087,31 @@ static const void* round_fn(bool store) {
 }
 
 template <int RK, int MODE, bool GATED>
-static const void* round_fn(bool small, bool store) {
-    return small ? round_fn<RK, MODE, GATED, 1>(store) : round_fn<RK, MODE, GATED, 16>(store);
+static const void* round_fn(int form, bool store) {
+    return form == kRowsSmall  ? round_fn<RK, MODE, GATED, 1>(store)
+           : form == kRowsHalf ? round_fn<RK, MODE, GATED, 8>(store)
+                               : round_fn<RK, MODE, GATED, 16>(store);
 }
 
 template <int RK>
-static const void* round_fn(bool sample, bool gated, bool small, bool store) {
-    if (sample) return gated ? round_fn<RK, kModeSample, true>(small, store) : round_fn<RK, kModeSample, false>(small, store);
-    return gated ? round_fn<RK, kModeGreedy, true>(small, store) : round_fn<RK, kModeGreedy, false>(small, store);
+static const void* round_fn(bool sample, bool gated, int form, bool store) {
+    if (sample) return gated ? round_fn<RK, kModeSample, true>(form, store) : round_fn<RK, kModeSample, false>(form, store);
+    return gated ? round_fn<RK, kModeGreedy, true>(form, store) : round_fn<RK, kModeGreedy, false>(form, store);
 }
 
-static const void* round_fn_r(int r, bool sample, bool gated, bool small, bool store) {
+static const void* round_fn_r(int r, bool sample, bool gated, int form, bool store) {
     switch (r / 16) {
-        case 1: return round_fn<1>(sample, gated, small, store);
-        case 2: return round_fn<2>(sample, gated, small, store);
-        case 4: return round_fn<4>(sample, gated, small, store);
-        case 8: return round_fn<8>(sample, gated, small, store);
-        case 16: return round_fn<16>(sample, gated, small, store);
+        case 1: return round_fn<1>(sample, gated, form, store);
+        case 2: return round_fn<2>(sample, gated, form, store);
+        case 4: return round_fn<4>(sample, gated, form, store);
+        case 8: return round_fn<8>(sample, gated, form, store);
+        case 16: return round_fn<16>(sample, gated, form, store);
         default: return nullptr;
     }
 }
 
-int round_max_coresident(int r, bool sample, bool gated, bool small, bool store) {
-    const void* fn = round_fn_r(r, sample, gated, small, store);
+int round_max_coresident(int r, bool sample, bool gated, int form, bool store) {
+    const void* fn = round_fn_r(r, sample, gated, form, store);
     int per_cu = 0;
     if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kRoundThreads, 0) != hipSuccess) return 0;
     return per_cu * device_cu_count();
@@ -1036,7 +1125,7 @@ int round_max_coresident(int r, bool sample, bool gated, bool small, bool store)
 // failure in the error word (tokens -1).  `cooperative` selects the guaranteed launch instead.
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool cooperative, hipStream_t st,
                                hipEvent_t ev_begin, hipEvent_t ev_end) {
-    const void* fn = round_fn_r(a.r, sample, gated, round_small_block(a.B), a.logits_out != nullptr);
+    const void* fn = round_fn_r(a.r, sample, gated, round_row_form(a.B), a.logits_out != nullptr);
     if (!fn) return hipErrorInvalidValue;
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
     RoundArgs copy = a;

@@ -36,8 +36,9 @@ def _rand_H(B, K, r, seed=0):
 SHAPES = [
     (8, 3, 3000, 256, S.BF16),   # the largest small block (at most 8 rows), ragged vocabulary tail
     (2, 2, 2050, 128, S.BF16),
-    (9, 2, 1000, 256, S.BF16),   # the smallest batch on the full 128-row block
-    (64, 2, 3000, 256, S.BF16),  # half a row block, ragged vocabulary tail
+    (9, 2, 1000, 256, S.BF16),   # the smallest half block (9 .. 64 rows: two sets of consumer waves)
+    (64, 2, 3000, 256, S.BF16),  # the largest half block, ragged vocabulary tail
+    (65, 2, 1500, 256, S.BF16),  # the smallest batch on the full 128-row block
     (40, 2, 2000, 64, S.BF16),
     (1, 4, 512, 16, S.F32),
     (3, 3, 1000, 16, S.BF16),
