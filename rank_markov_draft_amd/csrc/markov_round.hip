@@ -35,10 +35,10 @@
 //  * A ninth wave per workgroup (the finalizer) clears the pick words and counters at the start of the launch
 //    and, one position behind, merges the log-sum-exp partials of its rows into tokens and log-probabilities,
 //    so a round is a single launch.
-//  * A batch of at most 8 rows takes a small-block form: one U unit per item instead of sixteen, so the
-//    producers keep six items in flight and the ring has eight stages (a stream of W2-only items is bound by
-//    the bytes in flight), and (without the gate) the four consumer waves each take every fourth tile of a
-//    position for the same rows, handing their per-row results to wave 0 through LDS.  A batch of 9 .. 64
+//  * A batch of at most 8 rows takes a small-block form: one U unit per item instead of sixteen and eight ring
+//    stages, and (without the gate) two consumer waves that each take every other tile of a position for the
+//    same rows, handing their per-row results to wave 0 through LDS, with six producer waves of ten items in
+//    flight each (a stream of W2-only items is bound by the bytes in flight).  A batch of 9 .. 64
 //    rows takes a half-block form the same way: eight U units per item, five stages, and two sets of two
 //    consumer waves taking every other tile, so no consumer wave idles on rows past the batch.
 //  * The gated gather X = bf16(W1[a] (.) H) runs in four phases whose loads are all issued before their
@@ -71,16 +71,23 @@ struct Ring {
     static constexpr int kURow = 4 * kRTileV + 16;          // one U row of the tile (32 floats) + 16-byte pad
     static constexpr int kUBytes = 8 * UR * kURow;          // 8 UR rows
     static constexpr int kStage = kW2Bytes + kUBytes;
-    // one item = RK W2 units (64 lanes x 16 B) + UR U units (8 rows x 128 B); producer p takes units p, p + 4, ...
+    // one item = RK W2 units (64 lanes x 16 B) + UR U units (8 rows x 128 B); producer p of P takes units p, p + P, ...
     static constexpr int kUnits = RK + UR;
-    static constexpr int kUnitsPerProducer = (kUnits + 3) / 4;
     static constexpr int kDepth = HL ? 4 : UR == 1 ? 6 : 3;  // items in flight per producer, in registers
 };
 
-constexpr int kConsumers = 4;
-constexpr int kProducers = 4;
-constexpr int kFinalizers = 1;
-constexpr int kRoundThreads = 64 * (kConsumers + kProducers + kFinalizers);
+// Waves of a workgroup: consumers, producers and one finalizer, nine in all.  The ungated small block (at most 8
+// rows) has little consumer work per item, and its stream of W2-only items is bound by the bytes in flight, so it
+// runs two consumer waves and six producers with ten items in flight each (170 KB per CU, against 102 KB with
+// four producers of six items).
+template <int UR, bool GATED>
+struct Waves {
+    static constexpr bool kDeep = UR == 1 && !GATED;
+    static constexpr int kConsumers = kDeep ? 2 : 4;
+    static constexpr int kProducers = kDeep ? 6 : 4;
+    static constexpr int kDepth = kDeep ? 10 : 0;  // 0: the ring's own depth
+};
+constexpr int kRoundThreads = 64 * 9;
 
 // vmcnt waits with compile-time counts (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
 template <int N>
@@ -238,18 +245,20 @@ template <int RK, int MODE, bool GATED, int UR, bool STORE = false>
 __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArgs a) {
     // The gated half block keeps the gate rows of the next position in LDS (filled by the finalizer wave while the
     // current position streams), so the gather after a grid barrier waits on the W1 rows only.
+    constexpr int kConsumers = Waves<UR, GATED>::kConsumers;
+    constexpr int kProducers = Waves<UR, GATED>::kProducers;
+    static_assert(64 * (kConsumers + kProducers + 1) == kRoundThreads, "nine waves");
     constexpr bool HLDS = GATED && UR == 8;
     constexpr int kHPitch = 16 * RK + 4;  // floats per gate row in LDS (16-byte shift per row: no bank conflicts)
     using RG = Ring<RK, UR, HLDS>;
     constexpr bool SAMPLE = MODE == kModeSample;
-    // Consumer sets: a small block (at most 8 rows) leaves three of the four consumer waves without rows, so
-    // each wave instead forms a set of its own on the same 32 rows and takes every fourth tile of a position
-    // (slots s, s + 4, ...), handing its per-row results to set 0 through LDS at the end of the position (the
-    // greedy maximum and the block race are both maxima over tiles, merged in set order).  A half block (9 ..
-    // 64 rows) runs two sets of two waves the same way, taking every other tile.  The gated small block keeps
-    // one set: its gather holds more registers, and with the hand-over code it would spill at three waves per
-    // SIMD.
-    constexpr int SETS = UR == 8 ? 2 : (UR == 1 && !GATED) ? 4 : 1;
+    // Consumer sets: a small block (at most 8 rows) fills only one wave's 32 rows, so each of its two consumer
+    // waves forms a set of its own on the same rows and takes every other tile of a position (slots s, s + 2,
+    // ...), handing its per-row results to set 0 through LDS at the end of the position (the greedy maximum and
+    // the block race are both maxima over tiles, merged in set order).  A half block (9 .. 64 rows) runs two sets
+    // of two waves the same way.  The gated small block keeps one set of four waves: its gather holds more
+    // registers, and with the hand-over code it would spill at three waves per SIMD.
+    constexpr int SETS = UR == 8 ? 2 : (UR == 1 && !GATED) ? kConsumers : 1;
     constexpr int kRowWaves = kConsumers / SETS;  // consumer waves of one set (32 rows each)
     __shared__ __attribute__((aligned(1024))) uint8_t ring[RG::kNS * RG::kStage];
     __shared__ uint32_t ready[RG::kNS];  // +1 per producer per filled stage
@@ -399,8 +408,8 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         // stage layout the consumers read.  Unit u of an item: u < RK is W2 rows 2u .. (64 lanes x 16 B of the
         // tile's [32, r] block); u >= RK is U row group u - RK (8 rows x 32 floats).
         const int p = wave - kConsumers;
-        constexpr int NU = RG::kUnitsPerProducer;
-        constexpr int D = RG::kDepth;
+        constexpr int NU = (RG::kUnits + kProducers - 1) / kProducers;  // units per producer and item
+        constexpr int D = Waves<UR, GATED>::kDepth ? Waves<UR, GATED>::kDepth : RG::kDepth;
         u32x4_t regs[D][NU];
         // Per-lane parts of every unit's global and LDS addresses, computed once: a load then costs one 64-bit
         // add per unit (index arithmetic per item, with its 64-bit multiplies, took issue cycles from the
@@ -414,7 +423,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
         uint32_t soff[NU];   // byte offset in a stage
 #pragma unroll
         for (int n = 0; n < NU; ++n) {
-            const int u = p + 4 * n;
+            const int u = p + kProducers * n;
             if (u < RK) {
                 const int P = u * 64 + lane;
                 const int rho = P / (2 * RK), c = P % (2 * RK);
@@ -434,7 +443,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                     const uint8_t* ub = reinterpret_cast<const uint8_t*>(a.U + (size_t)lk * a.u_kstride + (size_t)b0 * a.u_stride + v0);
 #pragma unroll
                     for (int n = 0; n < NU; ++n) {
-                        const int u = p + 4 * n;
+                        const int u = p + kProducers * n;
                         // W2 is re-read every position: a cacheable load lets it stay in the last-level cache
                         if (u < RK)
                             dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
@@ -445,7 +454,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                     // a tile past the vocabulary's end or a row block past the batch: clamped rows and columns
 #pragma unroll
                     for (int n = 0; n < NU; ++n) {
-                        const int u = p + 4 * n;
+                        const int u = p + kProducers * n;
                         if (u < RK) {
                             const int P = u * 64 + lane;
                             const int vrow = min(v0 + P / (2 * RK), a.V - 1);
@@ -464,7 +473,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
                 const bool vfull = v0 + kRTileV <= a.V;
 #pragma unroll
                 for (int n = 0; n < NU; ++n) {
-                    const int u = p + 4 * n;
+                    const int u = p + kProducers * n;
                     if (u < RK) {
                         if (vfull) {
                             dst[n] = *reinterpret_cast<const u32x4_t*>(w2b + (size_t)(u * (64 / (2 * RK)) * r * 2) + w2lane);
@@ -497,7 +506,7 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
             uint8_t* st = ring + (i % RG::kNS) * RG::kStage;
 #pragma unroll
             for (int n = 0; n < NU; ++n) {
-                if (p + 4 * n < RG::kUnits) *reinterpret_cast<u32x4_t*>(st + soff[n]) = src[n];
+                if (p + kProducers * n < RG::kUnits) *reinterpret_cast<u32x4_t*>(st + soff[n]) = src[n];
                 if (UR == 16 && n % 2 == 1 && n + 1 < NU) __builtin_amdgcn_s_sleep(3);
             }
         };
