@@ -224,7 +224,9 @@ def test_full_serving_round_kernel_logits(D, serving):
     del logits
 
 
-ROUND_SHAPES = [(8, 3, 3000, 256), (3, 2, 1000, 32), (130, 2, 776, 64), (128, 3, 4096, 256), (40, 2, 2000, 128)]
+ROUND_SHAPES = [(8, 3, 3000, 256), (3, 2, 1000, 32), (130, 2, 776, 64), (128, 3, 4096, 256), (40, 2, 2000, 128),
+                # half blocks: five positions through the gate-row buffer at r = 256; a single position
+                (64, 5, 3000, 256), (9, 1, 1000, 256)]
 
 
 @pytest.mark.parametrize("shape", ROUND_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d" % s)
