@@ -1,6 +1,7 @@
 """GPU parity of the Selector path (dspark_topk, dspark_selector_draft) and of the gate (dspark_gate)."""
 import numpy as np
 import pytest
+import torch
 
 import oracle as O
 import synth as S
@@ -148,6 +149,29 @@ def test_full_selector_all_rows(D, mode):
     ref = O.selector_draft(w.U, w.W1, w.W2T, w.anchor, topk=16, mode=mode, seed=w.noise_seed, rows=rows)
     assert np.abs(scores[rows] - ref["tables"][rows]).max() <= 1e-3
     _restricted_check(D, w, w.W1, w.W2T, None, cand, tok, lp, mode, w.noise_seed, T, f"full selector {mode}")
+
+
+@pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
+@pytest.mark.parametrize("cfg", ["small", "full"])
+def test_gated_selector_with_unit_gate_is_the_markov_head_on_the_candidates(D, mode, cfg):
+    """H = 1: the gated Selector is the (ungated) Markov head restricted to the same candidates (equivalence page,
+    "The equivalence: remove the gate, recover the Markov Head").  The gated tables equal the ungated ones bit for
+    bit (a bf16 row times 1 is itself), so do the drafts, and both follow the oracle's restricted head."""
+    if cfg == "full":
+        w = S.workload("selector", mode=mode)
+    else:
+        w = S.strong("selector", B=6, K=5, V=3000, r=64, mode=mode)
+    T = 0.8 if mode == S.SAMPLE else 1.0
+    args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
+    kw = dict(topk=16, mode=mode, seed=5, temperature=T, want_cand=True, want_scores=True)
+    a = D.dspark_selector_draft(*args, **kw)
+    ones = torch.ones((w.B, w.K, w.r), dtype=torch.float32, device="cuda")
+    b = D.dspark_selector_draft(*args, H=ones, **kw)
+    for key in ("cand", "scores", "tokens", "logprobs"):
+        assert np.array_equal(host(a[key]), host(b[key])), key
+    tok, lp, cand = host(b["tokens"]), host(b["logprobs"]), host(b["cand"])
+    rows = None if cfg == "small" else [0, 64, 127]
+    _restricted_check(D, w, w.W1, w.W2T, None, cand, tok, lp, mode, 5, T, f"unit gate {cfg}", rows=rows)
 
 
 # -------------------------------------------------------------------------------------------- gate
