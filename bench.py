@@ -500,10 +500,11 @@ def main():
         tiny_head(), tiny_sel()
         tms, _ = timed_rounds(tiny_head, 20, flush=False)
         tsms, _ = timed_rounds(tiny_sel, 20, flush=False)
+        _, _, _, nl, _ = D.dspark_markov_draft_timed(U, W1t, W2t, anc, w2_layout=D.DSPARK_W2_RV, workspace=tws)
         extras["tiny_latency"] = {"workload": "B=1, K=4, V=512, r=16, fp32, greedy",
                                   "markov_draft_us": round(1e3 * float(tms.mean()), 1),
                                   "selector_topk_V_us": round(1e3 * float(tsms.mean()), 1),
-                                  "kernel_launches": {"markov_draft": 2 * w.K, "selector": 3}}
+                                  "kernel_launches": {"markov_draft": nl, "selector": 3}}
         del U
         torch.cuda.empty_cache()
 

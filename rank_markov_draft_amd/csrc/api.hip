@@ -311,6 +311,37 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
         }
     }
     if (logits_out) return fail(DSPARK_EUNSUPPORTED, "this shape does not take the whole-round kernel");
+    if ((size_t)V * r <= kValuRoundMaxVR) {
+        // a small problem: the whole round in one launch on the vector ALUs (it also clears the error word)
+        RoundValuArgs a{};
+        a.U = U;
+        a.W1 = W1;
+        a.W2 = W2use;
+        a.sj = (layout == DSPARK_W2_RV) ? V : 1;
+        a.sv = (layout == DSPARK_W2_RV) ? 1 : r;
+        a.anchor = anchor;
+        a.H = H;
+        a.B = B;
+        a.K = K;
+        a.V = V;
+        a.r = r;
+        a.k0 = k0;
+        a.c = kLog2e / teff;
+        a.inv_t = 1.0f / teff;
+        a.tokens = tokens;
+        a.logprobs = logprobs;
+        a.error = ws.counters + kErrorWord;
+        if (ev) (void)hipEventRecord(ev[0], st);
+        hipError_t e = launch_markov_round_valu(a, wdtype == DSPARK_BF16, sample, H != nullptr, st);
+        if (ev) (void)hipEventRecord(ev[1], st);
+        if (e != hipSuccess) return device_fail(e, "draft round launch");
+        if (kernel_launches) *kernel_launches = 1;
+        if (cf) {
+            e = launch_confidence(*cf, B, st);
+            if (e != hipSuccess) return device_fail(e, "confidence launch");
+        }
+        return DSPARK_OK;
+    }
     {
         // this path has no bounded waits: clear the error word so dspark_markov_status reports this call
         hipError_t e = launch_fill_u32(ws.counters + kErrorWord, 0u, 1, st);

@@ -50,6 +50,27 @@ struct StepArgsValu {
     float* logits_out;
 };
 
+// The whole draft round for small problems on the vector-ALU path (one launch, one workgroup per kValuRows rows
+// covering the whole vocabulary at every position).
+struct RoundValuArgs {
+    const float* U;         // [B, K, V]
+    const void* W1;         // [V, r]
+    const void* W2;         // [r, V] (sj = V, sv = 1) or [V, r] (sj = 1, sv = r)
+    int64_t sj, sv;
+    const int32_t* anchor;  // [B]
+    const float* H;         // [B, K, r] or null
+    int B, K, V, r;
+    uint32_t k0;
+    float c;                // log2(e) / T
+    float inv_t;            // 1 / T (1 in greedy mode)
+    int32_t* tokens;        // [B, K]
+    float* logprobs;        // [B, K] or null
+    uint32_t* error;        // the workspace's error word (cleared: this path has no bounded waits)
+};
+// Largest V * r the one-launch vector-ALU round takes (each workgroup reads the whole W2 every position).
+constexpr size_t kValuRoundMaxVR = 65536;
+hipError_t launch_markov_round_valu(const RoundValuArgs& a, bool bf16, bool sample, bool gated, hipStream_t st);
+
 struct ReduceArgs {
     Partials part;
     int G, Bpad;

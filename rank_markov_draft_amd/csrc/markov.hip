@@ -417,6 +417,154 @@ __global__ void __launch_bounds__(kThreads) markov_step_valu(StepArgsValu a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// The whole round for small problems (V r <= kValuRoundMaxVR, shapes the matrix-core round kernel does not
+// take): one workgroup per kValuRows rows covers the whole vocabulary at every position, so the K positions
+// run in one launch, each row's predecessor kept in LDS.  Per position the arithmetic is markov_step_valu's
+// over a single vocabulary span; the workgroup's threads are then merged as markov_reduce merges partials.
+// ------------------------------------------------------------------------------------------------
+template <typename WT, int MODE, bool GATED>
+__global__ void __launch_bounds__(kThreads) markov_round_valu(RoundValuArgs a) {
+    constexpr bool SAMPLE = MODE == kModeSample;
+    extern __shared__ float xs[];  // [kValuRows][r]
+    __shared__ int s_prev[kValuRows];
+    __shared__ float rk[kThreads / 64], rl[kThreads / 64], rm[kThreads / 64], rs[kThreads / 64];
+    __shared__ int ri[kThreads / 64];
+    const WT* W1 = reinterpret_cast<const WT*>(a.W1);
+    const WT* W2 = reinterpret_cast<const WT*>(a.W2);
+    const int r = a.r;
+    const int g16 = threadIdx.x & 15;
+    const int b0 = blockIdx.x * kValuRows;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.error) *a.error = 0u;
+    if (threadIdx.x < kValuRows)
+        s_prev[threadIdx.x] = b0 + (int)threadIdx.x < a.B ? min(max(a.anchor[b0 + threadIdx.x], 0), a.V - 1) : 0;
+    __syncthreads();
+    for (int k = 0; k < a.K; ++k) {
+        for (int i = threadIdx.x; i < kValuRows * r; i += kThreads) {
+            const int rb = i / r, j = i % r;
+            const int b = b0 + rb;
+            float x = 0.f;
+            if (b < a.B) {
+                x = wload<WT>(W1, (size_t)s_prev[rb] * r + j);
+                if (GATED) x *= a.H[((size_t)b * a.K + k) * r + j];
+            }
+            xs[i] = x;
+        }
+        __syncthreads();
+
+        float bk[kValuRows], bl[kValuRows], m[kValuRows], s[kValuRows];
+        int bi[kValuRows];
+        uint32_t k2[kValuRows];
+#pragma unroll
+        for (int rb = 0; rb < kValuRows; ++rb) {
+            bk[rb] = -INFINITY;
+            bl[rb] = 0.f;
+            m[rb] = kMinFinite;
+            s[rb] = 0.f;
+            bi[rb] = 0x7FFFFFFF;
+            k2[rb] = SAMPLE ? noise_key2(a.k0, (uint32_t)(b0 + rb), (uint32_t)k) : 0u;
+        }
+        // every thread runs the same iterations (the sampling race works on groups of 16 lanes)
+        for (int v0 = 0; v0 < a.V; v0 += kThreads) {
+            const int v = v0 + threadIdx.x;
+            const bool inr = v < a.V;
+            float acc[kValuRows] = {};
+            if (inr) {
+                for (int j = 0; j < r; ++j) {
+                    const float w = wload<WT>(W2, (size_t)j * a.sj + (size_t)v * a.sv);
+#pragma unroll
+                    for (int rb = 0; rb < kValuRows; ++rb) acc[rb] = fmaf(xs[rb * r + j], w, acc[rb]);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < kValuRows; ++rb) {
+                const int b = b0 + rb;
+                if (b >= a.B) continue;  // uniform over the workgroup
+                const float l = inr ? acc[rb] + a.U[((size_t)b * a.K + k) * a.V + v] : 0.f;
+                const float t = inr ? l * a.c : -INFINITY;
+                const float mn = fmaxf(m[rb], t);
+                s[rb] = s[rb] * fast_exp2(m[rb] - mn) + fast_exp2(t - mn);
+                m[rb] = mn;
+                if (SAMPLE) {
+                    float M = t;
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+                    const float e = inr ? fast_exp2(t - M) : 0.f;
+                    float P = e;
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) {
+                        const float y = __shfl_up(P, off, 16);
+                        if (g16 >= off) P += y;
+                    }
+                    const float S = __shfl(P, 15, 16);
+                    if (S > 0.f) {
+                        float E, target;
+                        block_race_variates(k2[rb], (uint32_t)((v - g16) / 16), S, E, target);
+                        const unsigned long long below = __ballot(P <= target && g16 < 15);
+                        const int sel = __popcll((below >> (threadIdx.x & 48)) & 0x7FFFull);
+                        const float key = fast_log2(S) + M - fast_log2(E);
+                        const float lsel = __shfl(l, sel, 16);
+                        if (key > bk[rb]) {
+                            bk[rb] = key;
+                            bi[rb] = v - g16 + sel;
+                            bl[rb] = lsel;
+                        }
+                    }
+                } else if (inr && l > bk[rb]) {
+                    bk[rb] = l;
+                    bi[rb] = v;
+                    bl[rb] = l;
+                }
+            }
+        }
+        // per row: the wave's lanes merged by shuffles, then the four waves in order through LDS
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int rb = 0; rb < kValuRows; ++rb) {
+            if (b0 + rb >= a.B) break;  // uniform over the workgroup
+            float kk = bk[rb], ll = bl[rb], mm = m[rb], ss = s[rb];
+            int ii = bi[rb];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const float ok_ = __shfl_xor(kk, off);
+                const int oi = __shfl_xor(ii, off);
+                const float ol = __shfl_xor(ll, off);
+                const float om = __shfl_xor(mm, off);
+                const float os = __shfl_xor(ss, off);
+                if (beats(ok_, oi, kk, ii)) {
+                    kk = ok_;
+                    ii = oi;
+                    ll = ol;
+                }
+                lse_merge(mm, ss, om, os);
+            }
+            if (lane == 0) {
+                rk[wave] = kk;
+                ri[wave] = ii;
+                rl[wave] = ll;
+                rm[wave] = mm;
+                rs[wave] = ss;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                for (int w = 1; w < kThreads / 64; ++w) {
+                    if (beats(rk[w], ri[w], kk, ii)) {
+                        kk = rk[w];
+                        ii = ri[w];
+                        ll = rl[w];
+                    }
+                    lse_merge(mm, ss, rm[w], rs[w]);
+                }
+                const size_t o = (size_t)(b0 + rb) * a.K + k;
+                a.tokens[o] = ii;
+                if (a.logprobs) a.logprobs[o] = ll * a.inv_t - (mm + fast_log2(ss)) * kLn2;
+                s_prev[rb] = min(max(ii, 0), a.V - 1);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Cross-workgroup reduction: one workgroup per row merges the G partials and writes the pick.
 // ------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads) markov_reduce(ReduceArgs a) {
@@ -534,6 +682,25 @@ hipError_t launch_markov_step_valu(const StepArgsValu& a, bool bf16, int mode, b
     const size_t shm = sizeof(float) * kValuRows * a.r;
     if (bf16) launch_valu_wt<uint16_t>(a, mode, gated, grid, shm, st);
     else launch_valu_wt<float>(a, mode, gated, grid, shm, st);
+    return hipGetLastError();
+}
+
+template <typename WT, int MODE>
+static void launch_round_valu_mode(const RoundValuArgs& a, bool gated, dim3 grid, size_t shm, hipStream_t st) {
+    if (gated) hipLaunchKernelGGL((markov_round_valu<WT, MODE, true>), grid, dim3(kThreads), shm, st, a);
+    else hipLaunchKernelGGL((markov_round_valu<WT, MODE, false>), grid, dim3(kThreads), shm, st, a);
+}
+
+hipError_t launch_markov_round_valu(const RoundValuArgs& a, bool bf16, bool sample, bool gated, hipStream_t st) {
+    const dim3 grid((a.B + kValuRows - 1) / kValuRows);
+    const size_t shm = sizeof(float) * kValuRows * a.r;
+    if (bf16) {
+        if (sample) launch_round_valu_mode<uint16_t, kModeSample>(a, gated, grid, shm, st);
+        else launch_round_valu_mode<uint16_t, kModeGreedy>(a, gated, grid, shm, st);
+    } else {
+        if (sample) launch_round_valu_mode<float, kModeSample>(a, gated, grid, shm, st);
+        else launch_round_valu_mode<float, kModeGreedy>(a, gated, grid, shm, st);
+    }
     return hipGetLastError();
 }
 
