@@ -87,10 +87,14 @@ def test_draft_parity(D, shape, mode, strength):
     check_draft(tok, lp, ref, what=f"{shape} {mode} {strength}")
 
 
-@pytest.mark.parametrize("B,V", [(9, 900), (4, 20000)], ids=["B9", "B4-small-block"])
+@pytest.mark.parametrize("B,V,r,wd", [(9, 900, 64, S.BF16), (4, 20000, 64, S.BF16), (6, 700, 24, S.F32),
+                                      (5, 1001, 48, S.BF16)],
+                         ids=["B9-half-block", "B4-small-block", "B6-f32-small-round", "B5-r48-small-round"])
 @pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
-def test_draft_gated_and_rv_layout(D, mode, B, V):
-    w = S.strong("gated", B=B, K=4, V=V, r=64, D=0, mode=mode)
+def test_draft_gated_and_rv_layout(D, mode, B, V, r, wd):
+    """The gated head with W2 stored [r, V]: the matrix-core round kernel (a transposed copy of W2 first) and the
+    one-launch vector-ALU round (fp32 weights, a rank that is not a power-of-two multiple of 16)."""
+    w = S.strong("gated", B=B, K=4, V=V, r=r, D=0, mode=mode, wdtype=wd)
     H = _rand_H(w.B, w.K, w.r, seed=3)
     tok, lp = D.dspark_markov_draft(t_f32(w.U), t_w(w.W1), t_w(w.W2), t_i32(w.anchor), w2_layout=D.DSPARK_W2_RV,
                                     H=t_f32(H), mode=mode, seed=11)
