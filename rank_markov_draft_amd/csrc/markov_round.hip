@@ -276,7 +276,12 @@ __global__ void __launch_bounds__(kRoundThreads, 1) markov_round_kernel(RoundArg
     __shared__ uint32_t mput[kHand][kRowWaves], mgot[kHand][kRowWaves];  // segments written / read
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // In the half block the wave index is made wave-uniform, so the hand-over slots and counters of the consumer
+    // sets and the release address live in scalar registers: held as per-lane values at 168 registers they
+    // spilled, and every reload after a position's last tile was a memory round trip under the stream (gated
+    // sampling round 0.383 -> 0.353 ms, greedy 0.351 -> 0.348 ms, same-box A/B).  Other forms keep the plain
+    // index, which measured faster there (batch-1 sampling 0.245 against 0.247 ms).
+    const int wave = UR == 8 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
     const int half = lane >> 5;
     const int G = gridDim.x;
     const int g = blockIdx.x;
