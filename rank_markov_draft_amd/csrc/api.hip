@@ -264,9 +264,18 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
                           (!g_cooperative.load(std::memory_order_relaxed) || coop_supported());
     if (round_ok) {
         const int ntiles = (V + 31) / 32;
-        int G = round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
-        if (G > round_gmax()) G = round_gmax();
-        if (G > ntiles) G = ntiles;
+        // a single row at r = 256 (greedy) keeps W2 resident on chip instead of streaming it at every position
+        int Gres = 0;
+        if (B == 1 && r == 256 && !sample) {
+            Gres = resident_max_coresident(H != nullptr, logits_out != nullptr);
+            if (Gres > round_gmax()) Gres = round_gmax();
+        }
+        const bool resident = resident_supported(B, r, sample, V, Gres);
+        int G = resident ? Gres : round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
+        if (!resident) {
+            if (G > round_gmax()) G = round_gmax();
+            if (G > ntiles) G = ntiles;
+        }
         if (G >= 1) {
             RoundArgs a{};
             a.U = U;
@@ -303,8 +312,9 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.p_idx = ws.p_idx;
             a.p_l = ws.p_l;
             a.logits_out = logits_out;
-            hipError_t e = launch_markov_round(a, sample, H != nullptr, g_cooperative.load(std::memory_order_relaxed) != 0,
-                                               st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+            const bool coop = g_cooperative.load(std::memory_order_relaxed) != 0;
+            hipError_t e = resident ? launch_markov_resident(a, H != nullptr, coop, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)
+                                    : launch_markov_round(a, sample, H != nullptr, coop, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
             if (e != hipSuccess) return device_fail(e, "draft round launch");
             if (kernel_launches) *kernel_launches = 1;
             return DSPARK_OK;

@@ -148,6 +148,13 @@ inline int round_row_form(int B) { return B <= 8 ? kRowsSmall : B <= 64 ? kRowsH
 int round_max_coresident(int r, bool sample, bool gated, int form, bool store = false);
 hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool cooperative, hipStream_t st,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
+// The resident round: a single row, r = 256, greedy; each lane keeps one vocabulary row of W2 in registers for the
+// whole round (workgroup g covers ids [g V / G, (g + 1) V / G), at most 640).  Same arguments and workspace as the
+// tiled round.
+int resident_max_coresident(bool gated, bool store);
+bool resident_supported(int B, int r, bool sample, int V, int G);
+hipError_t launch_markov_resident(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st, hipEvent_t ev_begin,
+                                  hipEvent_t ev_end);
 
 int mfma_supported_r(int r);
 hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);

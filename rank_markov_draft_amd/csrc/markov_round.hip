@@ -1084,6 +1084,243 @@ __global__ void __launch_bounds__(64) confidence_kernel(ConfArgs c) {
     for (int k = 0; k < c.K; ++k) confidence_step(c, blockIdx.x, k);
 }
 
+// ====================================================================================================================
+// The resident round: one row (B = 1), r = 256, greedy picks.
+//
+// A single row's draft with the tiled round streams all of W2 at every position (2 r V bytes, 77.8 MB at V = 151936)
+// to compute one row of logits.  Here each lane of ten waves per workgroup holds one vocabulary row of W2 (256 bf16
+// in 128 registers) for the whole round, read once at the start; a position then reads only its base logits, the
+// pick word and one W1 row (and gate row), and each lane forms its logit U_k[v] + W2[v] . X with v_dot2 on bf16
+// pairs against X broadcast from LDS.  Workgroup g covers the ids [g V / G, (g + 1) V / G), at most 640 of them.
+// The pick word, the log-sum-exp partials, the grid barrier and the finalizer's merge are the tiled round's.
+constexpr int kResWaves = 10;                       // waves holding W2 rows, one id per lane
+constexpr int kResThreads = 64 * (kResWaves + 1);   // and the finalizer
+constexpr int kResR = 256;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <bool GATED, bool STORE>
+__global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t xs[kResWaves][kResR / 2];  // each wave's copy of X (bf16 pairs)
+    // per wave and position: best logit, its id, base-2 max and sum of the log-sum-exp (read by the workgroup's last
+    // wave to finish the position, which merges them in wave order)
+    __shared__ float wkey[kResWaves], wmc[kResWaves], wsum[kResWaves];
+    __shared__ int wid[kResWaves];
+    __shared__ uint32_t released, stepdone;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const uint32_t spin_limit = a.spin_limit;
+    if (threadIdx.x == 0) {
+        released = 0u;
+        stepdone = 0u;
+    }
+    const uint64_t tag = launch_tag(a, agent_load(a.epoch));
+    __syncthreads();
+
+    if (wave == kResWaves) {
+        // ============================================================== finalizer (the row's owner: workgroup 0)
+        if (g != 0) return;
+        const size_t nw = (size_t)a.K * a.Bpad * kWinnerSlots;
+        for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i * kWinnerStride, 0ull);
+        if (lane < kBarrierGroups) {
+            agent_store(a.barrier + kCounterStride * lane, 0u);
+            agent_store(a.release + kCounterStride * lane, 0u);
+        }
+        if (lane == 0) {
+            agent_store(a.top, 0u);
+            agent_store(a.error, 0u);
+        }
+        wait_vmcnt<0>();
+        if (lane == 0) agent_store(a.flag, tag);
+        if (a.cf.h) confidence_step(a.cf, 0, 0);
+        for (int k = 0; k < a.K; ++k) {
+            bool timed_out = false;
+            uint32_t spins = 0;
+            if (k + 1 < a.K) {
+                while (lds_load(&released) < (uint32_t)(k + 1)) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > spin_limit) {
+                        timed_out = true;
+                        break;
+                    }
+                }
+            } else {
+                while (released_position(a) < (uint32_t)a.K) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > spin_limit) {
+                        timed_out = true;
+                        break;
+                    }
+                }
+            }
+            if (timed_out && lane == 0) agent_store(a.error, 1u);
+            finalize_pair(a, 0, k, timed_out);
+            if (a.cf.h && k + 1 < a.K) confidence_step(a.cf, 0, k + 1);
+        }
+        if (lane == 0) agent_store(a.epoch, agent_load(a.epoch) + 1u);
+        return;
+    }
+
+    // ================================================================== W2 rows resident in registers
+    const int v_lo = (int)(((int64_t)g * a.V) / G);
+    const int v_hi = (int)(((int64_t)(g + 1) * a.V) / G);
+    const int v = v_lo + 64 * wave + lane;
+    const bool live = v < v_hi;
+    u32x4_t w[kResR / 8];
+    {
+        const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)(live ? v : v_lo) * kResR);
+#pragma unroll
+        for (int q = 0; q < kResR / 8; ++q) w[q] = wp[q];
+    }
+    const float c = a.c;
+    float u_next = live ? a.U[v] : 0.f;
+    for (int k = 0; k < a.K; ++k) {
+        const float u_cur = u_next;
+        if (k + 1 < a.K) u_next = live ? a.U[(size_t)(k + 1) * a.u_kstride + v] : 0.f;
+        // the previous position's pick: wave 0 polls this workgroup's copy of the release word, the others its LDS flag
+        if (k > 0) {
+            uint32_t spins = 0;
+            if (wave == 0) {
+                while (released_position(a) < (uint32_t)k) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > spin_limit) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+                if (lane == 0) __hip_atomic_store(&released, (uint32_t)k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                while (lds_load(&released) < (uint32_t)k) {
+                    __builtin_amdgcn_s_sleep(0);
+                    if (++spins > spin_limit) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+        }
+        int pv;
+        if (k == 0) {
+            pv = a.anchor[0];
+        } else {
+            const unsigned long long wv = pick_word(a, k - 1, 0);
+            pv = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
+        }
+        pv = min(max(pv, 0), a.V - 1);
+        // X = W1[pv] (gated: bf16(W1[pv] * H[0, k])) into this wave's LDS copy, one 16-byte chunk per lane
+        if (lane < kResR / 8) {
+            u32x4_t raw = reinterpret_cast<const u32x4_t*>(a.W1 + (size_t)pv * kResR)[lane];
+            if constexpr (GATED) {
+                const float* hrow = a.H + (size_t)k * kResR + 8 * lane;
+                const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(hrow);
+                const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(hrow + 4);
+                const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
+                uint32_t o32[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_to_f32((uint16_t)(w32[e] & 0xFFFFu)) * hf[2 * e];
+                    const float hi = bf16_to_f32((uint16_t)(w32[e] >> 16)) * hf[2 * e + 1];
+                    o32[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                }
+                raw = u32x4_t{o32[0], o32[1], o32[2], o32[3]};
+            }
+            *reinterpret_cast<u32x4_t*>(&xs[wave][4 * lane]) = raw;
+        }
+        wait_lgkmcnt0();
+        __asm__ volatile("" ::: "memory");  // the wave's X writes land before its reads
+        // l = U_k[v] + W2[v] . X, two partial sums added in a fixed order
+        float acc0 = u_cur, acc1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < kResR / 8; ++q) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&xs[wave][4 * q]);
+            acc0 = dot2_bf16(w[q].x, x.x, acc0);
+            acc1 = dot2_bf16(w[q].y, x.y, acc1);
+            acc0 = dot2_bf16(w[q].z, x.z, acc0);
+            acc1 = dot2_bf16(w[q].w, x.w, acc1);
+        }
+        const float l = acc0 + acc1;
+        if constexpr (STORE) {
+            if (live) a.logits_out[(size_t)k * a.V + v] = l;
+        }
+        // the wave's pick (largest logit, lowest id on ties) and log-sum-exp terms
+        float bk = live ? l : -INFINITY;
+        int bi = live ? v : 0x7FFFFFFF;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ok = __shfl_xor(bk, off);
+            const int oi = __shfl_xor(bi, off);
+            if (beats(ok, oi, bk, bi)) {
+                bk = ok;
+                bi = oi;
+            }
+        }
+        const float mc = fmaxf(bk, kNegBig) * c;
+        float e = live ? fast_exp2(fmaf(l, c, -mc)) : 0.f;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+        if (k == 0 && lane == 0) wait_cleared(a, tag);  // this launch's counters before this wave's first arrival
+        if (lane == 0) {
+            wkey[wave] = bk;
+            wid[wave] = bi;
+            wmc[wave] = mc;
+            wsum[wave] = e;
+        }
+        wait_lgkmcnt0();
+        __asm__ volatile("" ::: "memory");
+        int last = 0;
+        if (lane == 0)
+            last = __hip_atomic_fetch_add(&stepdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+                   (uint32_t)kResWaves * (uint32_t)(k + 1) - 1u;
+        if (__shfl(last, 0)) {
+            // the workgroup's last wave: merge the waves in order, then the global pick, partials and arrival.  The
+            // lane index is formed here (the W2 rows leave no register to keep one across the loop)
+            __asm__ volatile("" ::: "memory");
+            int ln;
+            __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const bool has = ln < kResWaves;
+            const int j = has ? ln : 0;
+            float mk = has ? wkey[j] : -INFINITY;
+            int mi = has ? wid[j] : 0x7FFFFFFF;
+            float mm = has ? wmc[j] : kNegBig * c;
+            float ms = has ? wsum[j] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const float ok = __shfl_xor(mk, off);
+                const int oi = __shfl_xor(mi, off);
+                const float om = __shfl_xor(mm, off);
+                const float os = __shfl_xor(ms, off);
+                if (beats(ok, oi, mk, mi)) {
+                    mk = ok;
+                    mi = oi;
+                }
+                lse_merge(mm, ms, om, os);
+            }
+            if (lane == 0) {
+                const unsigned long long packed =
+                    ((unsigned long long)ordered_key(mk) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)mi);
+                atomicMax(a.winners + ((size_t)k * a.Bpad * kWinnerSlots + g % kWinnerSlots) * kWinnerStride, packed);
+                const size_t o = ((size_t)k * G + g) * a.Bpad;
+                agent_store(a.p_mc + o, mm);
+                agent_store(a.p_s + o, ms);
+                agent_store(a.p_idx + o, mi);
+                agent_store(a.p_l + o, mk);
+            }
+            wait_vmcnt<0>();
+            int last_all = 0;
+            if (lane == 0) last_all = arrive(a, k) ? 1 : 0;
+            if (__shfl(last_all, 0) && lane < kBarrierGroups)
+                agent_store(a.release + kCounterStride * lane, (uint32_t)(k + 1));
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_confidence(const ConfArgs& c, int B, hipStream_t st) {
@@ -1146,6 +1383,37 @@ hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool
     void* args[] = {&copy};
     const hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st)
                                      : hipLaunchKernel(fn, dim3(a.G), dim3(kRoundThreads), args, 0, st);
+    if (ev_end) (void)hipEventRecord(ev_end, st);
+    return e;
+}
+
+static const void* resident_fn(bool gated, bool store) {
+    return gated ? (store ? reinterpret_cast<const void*>(&markov_resident_kernel<true, true>)
+                          : reinterpret_cast<const void*>(&markov_resident_kernel<true, false>))
+                 : (store ? reinterpret_cast<const void*>(&markov_resident_kernel<false, true>)
+                          : reinterpret_cast<const void*>(&markov_resident_kernel<false, false>));
+}
+
+int resident_max_coresident(bool gated, bool store) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_fn(gated, store), kResThreads, 0) != hipSuccess) return 0;
+    return per_cu * device_cu_count();
+}
+
+bool resident_supported(int B, int r, bool sample, int V, int G) {
+    return B == 1 && r == kResR && !sample && G >= 1 && (int64_t)V <= (int64_t)kResWaves * 64 * G;
+}
+
+// Launched like the tiled round (one workgroup per CU, ordinary launch unless `cooperative`).
+hipError_t launch_markov_resident(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st, hipEvent_t ev_begin,
+                                  hipEvent_t ev_end) {
+    if (!resident_supported(a.B, a.r, false, a.V, a.G)) return hipErrorInvalidValue;
+    const void* fn = resident_fn(gated, a.logits_out != nullptr);
+    if (ev_begin) (void)hipEventRecord(ev_begin, st);
+    RoundArgs copy = a;
+    void* args[] = {&copy};
+    const hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kResThreads), args, 0, st)
+                                     : hipLaunchKernel(fn, dim3(a.G), dim3(kResThreads), args, 0, st);
     if (ev_end) (void)hipEventRecord(ev_end, st);
     return e;
 }

@@ -50,6 +50,8 @@ SHAPES = [
     (4, 2, 600, 48, S.BF16),
     (2, 2, 300, 512, S.BF16),  # r = 512: per-position kernels
     (7, 2, 257, 16, S.F32),
+    (1, 3, 3000, 256, S.BF16),  # one row at r = 256: greedy drafts keep W2 resident (most lanes hold no id)
+    (1, 2, 200, 256, S.BF16),   # fewer ids than workgroups: some workgroups hold none
 ]
 
 
@@ -88,8 +90,9 @@ def test_draft_parity(D, shape, mode, strength):
 
 
 @pytest.mark.parametrize("B,V,r,wd", [(9, 900, 64, S.BF16), (4, 20000, 64, S.BF16), (6, 700, 24, S.F32),
-                                      (5, 1001, 48, S.BF16)],
-                         ids=["B9-half-block", "B4-small-block", "B6-f32-small-round", "B5-r48-small-round"])
+                                      (5, 1001, 48, S.BF16), (1, 3000, 256, S.BF16)],
+                         ids=["B9-half-block", "B4-small-block", "B6-f32-small-round", "B5-r48-small-round",
+                              "B1-resident"])
 @pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
 def test_draft_gated_and_rv_layout(D, mode, B, V, r, wd):
     """The gated head with W2 stored [r, V]: the matrix-core round kernel (a transposed copy of W2 first) and the
@@ -230,7 +233,9 @@ def test_full_serving_round_kernel_logits(D, serving):
 
 ROUND_SHAPES = [(8, 3, 3000, 256), (3, 2, 1000, 32), (130, 2, 776, 64), (128, 3, 4096, 256), (40, 2, 2000, 128),
                 # half blocks: five positions through the gate-row buffer at r = 256; a single position
-                (64, 5, 3000, 256), (9, 1, 1000, 256)]
+                (64, 5, 3000, 256), (9, 1, 1000, 256),
+                # one row at r = 256 (greedy: the resident round), with empty workgroups in the second
+                (1, 3, 3000, 256), (1, 2, 200, 256)]
 
 
 @pytest.mark.parametrize("shape", ROUND_SHAPES, ids=lambda s: "B%d-K%d-V%d-r%d" % s)
@@ -286,6 +291,19 @@ def test_gate_ones_equals_ungated_at_full_shapes(D, cfg, mode):
 def test_full_batch1_greedy(D):
     w = S.workload("batch1")
     _full_draft_check(D, w, None, S.GREEDY, 0, what="batch-1 greedy")
+
+
+@pytest.mark.parametrize("extra", [0, 4], ids=["at-limit", "past-limit"])
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+def test_batch1_resident_vocabulary_limit(D, extra, gated):
+    """One row at r = 256, greedy: the resident round covers at most 640 ids per workgroup (one per lane of ten
+    waves), so V = 640 x CUs is its largest vocabulary; four ids more take the tiled round.  Both against the
+    oracle at every position."""
+    V = 640 * torch.cuda.get_device_properties(0).multi_processor_count + extra
+    w = S.workload("batch1", K=2, V=V)
+    H = _rand_H(1, 2, 256, seed=5) if gated else None
+    _full_draft_check(D, w, None, S.GREEDY, 0, H=None if H is None else t_f32(H),
+                      Hd=None if H is None else H.astype(np.float64), what=f"batch-1 V={V}")
 
 
 def test_cooperative_launch_matches_default(D):
