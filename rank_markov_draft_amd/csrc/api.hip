@@ -270,7 +270,7 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             Gres = resident_max_coresident(H != nullptr, logits_out != nullptr);
             if (Gres > round_gmax()) Gres = round_gmax();
         }
-        const bool resident = resident_supported(B, r, sample, V, Gres);
+        const bool resident = resident_supported(B, K, r, sample, V, Gres, ws.Bpad);
         int G = resident ? Gres : round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
         if (!resident) {
             if (G > round_gmax()) G = round_gmax();

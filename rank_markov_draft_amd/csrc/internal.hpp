@@ -150,9 +150,9 @@ hipError_t launch_markov_round(const RoundArgs& a, bool sample, bool gated, bool
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 // The resident round: a single row, r = 256, greedy; each lane keeps one vocabulary row of W2 in registers for the
 // whole round (workgroup g covers ids [g V / G, (g + 1) V / G), at most 640).  Same arguments and workspace as the
-// tiled round.
+// tiled round; its per-workgroup pick words of positions 0 .. K use the winner array.
 int resident_max_coresident(bool gated, bool store);
-bool resident_supported(int B, int r, bool sample, int V, int G);
+bool resident_supported(int B, int K, int r, bool sample, int V, int G, int Bpad);
 hipError_t launch_markov_resident(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st, hipEvent_t ev_begin,
                                   hipEvent_t ev_end);
 

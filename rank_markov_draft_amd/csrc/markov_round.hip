@@ -204,12 +204,11 @@ __device__ void confidence_step(const ConfArgs& c, int b, int k) {
     }
 }
 
-// One wave merges the G partials of (row b, position k): the pick from the winner word, the log-sum-exp over
+// One wave merges the G partials of (row b, position k): the pick from the winner word wv, the log-sum-exp over
 // the partials, the logit of the pick from the partial of the workgroup that owns its id.
-__device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) {
+__device__ void finalize_with(const RoundArgs& a, int b, int k, unsigned long long wv, bool timed_out) {
     const int lane = threadIdx.x & 63;
     const int G = a.G;
-    const unsigned long long wv = pick_word(a, k, b);
     const int tok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
     float mc = kMinFinite, s = 0.f, l = 0.f;
     int found = 0;
@@ -237,6 +236,10 @@ __device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) 
         agent_store(a.tokens + (size_t)b * a.K + k, bad ? -1 : tok);
         if (a.logprobs) a.logprobs[(size_t)b * a.K + k] = bad ? NAN : l * a.inv_t - (mc + fast_log2(s)) * kLn2;
     }
+}
+
+__device__ void finalize_pair(const RoundArgs& a, int b, int k, bool timed_out) {
+    finalize_with(a, b, k, pick_word(a, k, b), timed_out);
 }
 
 // STORE (validation only) also writes every tile's calibrated logits to a.logits_out [B, K, V] before its
@@ -1090,9 +1093,18 @@ __global__ void __launch_bounds__(64) confidence_kernel(ConfArgs c) {
 // A single row's draft with the tiled round streams all of W2 at every position (2 r V bytes, 77.8 MB at V = 151936)
 // to compute one row of logits.  Here each lane of ten waves per workgroup holds one vocabulary row of W2 (256 bf16
 // in 128 registers) for the whole round, read once at the start; a position then reads only its base logits, the
-// pick word and one W1 row (and gate row), and each lane forms its logit U_k[v] + W2[v] . X with v_dot2 on bf16
+// previous pick and one W1 row (and gate row), and each lane forms its logit U_k[v] + W2[v] . X with v_dot2 on bf16
 // pairs against X broadcast from LDS.  Workgroup g covers the ids [g V / G, (g + 1) V / G), at most 640 of them.
-// The pick word, the log-sum-exp partials, the grid barrier and the finalizer's merge are the tiled round's.
+//
+// With no stream to overlap, a position is a chain of memory round trips, so the hand-over is kept short: each
+// workgroup writes its packed (key, ~id) word for position k into a slot of its own (slot[k][g] in the winner
+// array, cleared at the start of the launch; a written word is never zero), and wave 0 of every workgroup polls
+// the G slots of position k until all are written and takes their maximum, the same pick the tiled round's atomic
+// maximum gives.  That replaces the atomic maximum, the arrival counters, the release word and the pick read by
+// one store and one polled read.  The log-sum-exp partials are written just before the slot word, and each wave
+// waits for all its stores at the next position before the workgroup's next slot word, so partials of position k
+// are complete once every slot of position k + 1 (or every done word after the last position) is written; the
+// finalizer of workgroup 0 merges them then, one position behind.
 constexpr int kResWaves = 10;                       // waves holding W2 rows, one id per lane
 constexpr int kResThreads = 64 * (kResWaves + 1);   // and the finalizer
 constexpr int kResR = 256;
@@ -1102,6 +1114,42 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// One wave: waits (bounded) until all G slot words of position k are written, then returns their maximum (0 and
+// *timed_out set if the wait gave up).
+__device__ unsigned long long resident_slots(const RoundArgs& a, int k, int G, bool* timed_out) {
+    constexpr int kPer = 1024 / 64;  // words per lane at the largest grid
+    const int lane = threadIdx.x & 63;
+    const unsigned long long* row = a.winners + (size_t)k * G;
+    uint32_t spins = 0;
+    while (true) {
+        // every word of a pass is requested before any is examined: one round trip per pass
+        unsigned long long wv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) wv[i] = (lane + 64 * i < G) ? agent_load(row + lane + 64 * i) : ~0ull;
+        unsigned long long best = 0ull;
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const bool used = lane + 64 * i < G;
+            all = all && wv[i] != 0ull;
+            best = (used && wv[i] > best) ? wv[i] : best;
+        }
+        if (__all(all)) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const unsigned long long o = __shfl_xor(best, off);
+                best = o > best ? o : best;
+            }
+            return best;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+            *timed_out = true;
+            return 0ull;
+        }
+    }
+}
+
 template <bool GATED, bool STORE>
 __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t xs[kResWaves][kResR / 2];  // each wave's copy of X (bf16 pairs)
@@ -1109,7 +1157,10 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
     // wave to finish the position, which merges them in wave order)
     __shared__ float wkey[kResWaves], wmc[kResWaves], wsum[kResWaves];
     __shared__ int wid[kResWaves];
-    __shared__ uint32_t released, stepdone;
+    // stepdone: waves done per position; donecnt: waves past the last position (a counter of its own, since a wave
+    // reaches it without waiting for the others); picked: positions whose pick the pick wave has placed in ptok
+    __shared__ uint32_t stepdone, donecnt, picked;
+    __shared__ int ptok;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1117,53 +1168,51 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
     const int g = blockIdx.x;
     const uint32_t spin_limit = a.spin_limit;
     if (threadIdx.x == 0) {
-        released = 0u;
         stepdone = 0u;
+        donecnt = 0u;
+        picked = 0u;
+        ptok = 0;
     }
     const uint64_t tag = launch_tag(a, agent_load(a.epoch));
     __syncthreads();
 
     if (wave == kResWaves) {
-        // ============================================================== finalizer (the row's owner: workgroup 0)
-        if (g != 0) return;
-        const size_t nw = (size_t)a.K * a.Bpad * kWinnerSlots;
-        for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i * kWinnerStride, 0ull);
-        if (lane < kBarrierGroups) {
-            agent_store(a.barrier + kCounterStride * lane, 0u);
-            agent_store(a.release + kCounterStride * lane, 0u);
+        // ============================================================== pick wave (and, in workgroup 0, finalizer)
+        // Polls the slot words of each position and hands the pick to this workgroup's waves through LDS; the
+        // waves that hold W2 rows have no registers to spare for a poll.  In workgroup 0 it then merges the
+        // previous position, whose partials are complete now (see above).
+        if (g == 0) {
+            const size_t nw = (size_t)(a.K + 1) * G;
+            for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i, 0ull);
+            if (lane == 0) agent_store(a.error, 0u);
+            wait_vmcnt<0>();
+            if (lane == 0) agent_store(a.flag, tag);
+            if (a.cf.h) confidence_step(a.cf, 0, 0);
+        } else if (lane == 0) {
+            wait_cleared(a, tag);  // no slot word is read before this launch has cleared it
         }
-        if (lane == 0) {
-            agent_store(a.top, 0u);
-            agent_store(a.error, 0u);
-        }
-        wait_vmcnt<0>();
-        if (lane == 0) agent_store(a.flag, tag);
-        if (a.cf.h) confidence_step(a.cf, 0, 0);
-        for (int k = 0; k < a.K; ++k) {
+        unsigned long long prev = 0ull;
+        bool prev_to = false;
+        // workgroup 0 follows every position and the done words; the others need the picks of 0 .. K - 2 only
+        const int kend = g == 0 ? a.K : a.K - 2;
+        for (int k = 0; k <= kend; ++k) {
             bool timed_out = false;
-            uint32_t spins = 0;
-            if (k + 1 < a.K) {
-                while (lds_load(&released) < (uint32_t)(k + 1)) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > spin_limit) {
-                        timed_out = true;
-                        break;
-                    }
-                }
-            } else {
-                while (released_position(a) < (uint32_t)a.K) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++spins > spin_limit) {
-                        timed_out = true;
-                        break;
-                    }
-                }
-            }
+            const unsigned long long wv = resident_slots(a, k, G, &timed_out);
             if (timed_out && lane == 0) agent_store(a.error, 1u);
-            finalize_pair(a, 0, k, timed_out);
-            if (a.cf.h && k + 1 < a.K) confidence_step(a.cf, 0, k + 1);
+            if (k + 1 < a.K && lane == 0) {
+                ptok = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
+                __hip_atomic_store(&picked, (uint32_t)(k + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            if (g == 0 && k >= 1) {
+                // c_k needs x_{k-1} only, so it follows the token of position k - 1 at once
+                finalize_with(a, 0, k - 1, prev, prev_to || timed_out);
+                if (a.cf.h && k < a.K) confidence_step(a.cf, 0, k);
+            }
+            prev = wv;
+            prev_to = timed_out;
         }
-        if (lane == 0) agent_store(a.epoch, agent_load(a.epoch) + 1u);
+        // every workgroup has written its done word, so all have read the epoch: advance it
+        if (g == 0 && lane == 0) agent_store(a.epoch, agent_load(a.epoch) + 1u);
         return;
     }
 
@@ -1180,37 +1229,36 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
     }
     const float c = a.c;
     float u_next = live ? a.U[v] : 0.f;
-    for (int k = 0; k < a.K; ++k) {
-        const float u_cur = u_next;
-        if (k + 1 < a.K) u_next = live ? a.U[(size_t)(k + 1) * a.u_kstride + v] : 0.f;
-        // the previous position's pick: wave 0 polls this workgroup's copy of the release word, the others its LDS flag
-        if (k > 0) {
-            uint32_t spins = 0;
-            if (wave == 0) {
-                while (released_position(a) < (uint32_t)k) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++spins > spin_limit) {
-                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-                if (lane == 0) __hip_atomic_store(&released, (uint32_t)k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            } else {
-                while (lds_load(&released) < (uint32_t)k) {
-                    __builtin_amdgcn_s_sleep(0);
-                    if (++spins > spin_limit) {
-                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-            }
+    for (int k = 0; k <= a.K; ++k) {
+        if (k == a.K) {
+            // after the last position: a done word once every wave's stores are complete
+            wait_vmcnt<0>();
+            int last = 0;
+            if (lane == 0)
+                last = __hip_atomic_fetch_add(&donecnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+                       (uint32_t)kResWaves - 1u;
+            if (lane == 0 && last) agent_store(a.winners + (size_t)k * G + g, 1ull);
+            break;
         }
+        const float u_cur = u_next;
+        if (k + 1 < a.K) {
+            const float* ub = a.U + (size_t)(k + 1) * a.u_kstride;  // wave-uniform base, 32-bit lane offset
+            u_next = live ? ub[(uint32_t)v] : 0.f;
+        }
+        // the previous position's pick, from the pick wave through LDS
         int pv;
         if (k == 0) {
             pv = a.anchor[0];
         } else {
-            const unsigned long long wv = pick_word(a, k - 1, 0);
-            pv = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
+            uint32_t spins = 0;
+            while (__hip_atomic_load(&picked, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)k) {
+                __builtin_amdgcn_s_sleep(0);
+                if (++spins > spin_limit) {
+                    __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            pv = ptok;
         }
         pv = min(max(pv, 0), a.V - 1);
         // X = W1[pv] (gated: bf16(W1[pv] * H[0, k])) into this wave's LDS copy, one 16-byte chunk per lane
@@ -1265,13 +1313,15 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
         float e = live ? fast_exp2(fmaf(l, c, -mc)) : 0.f;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
-        if (k == 0 && lane == 0) wait_cleared(a, tag);  // this launch's counters before this wave's first arrival
+        if (k == 0 && lane == 0) wait_cleared(a, tag);  // this launch's slot words are cleared before any is written
         if (lane == 0) {
             wkey[wave] = bk;
             wid[wave] = bi;
             wmc[wave] = mc;
             wsum[wave] = e;
         }
+        // this wave's stores of earlier positions (partials, slot word) are complete before the workgroup's next word
+        wait_vmcnt<0>();
         wait_lgkmcnt0();
         __asm__ volatile("" ::: "memory");
         int last = 0;
@@ -1279,8 +1329,8 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
             last = __hip_atomic_fetch_add(&stepdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
                    (uint32_t)kResWaves * (uint32_t)(k + 1) - 1u;
         if (__shfl(last, 0)) {
-            // the workgroup's last wave: merge the waves in order, then the global pick, partials and arrival.  The
-            // lane index is formed here (the W2 rows leave no register to keep one across the loop)
+            // the workgroup's last wave: merge the waves in order, then the partials and the slot word.  The lane
+            // index is formed here (the W2 rows leave no register to keep one across the loop)
             __asm__ volatile("" ::: "memory");
             int ln;
             __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
@@ -1303,20 +1353,15 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
                 lse_merge(mm, ms, om, os);
             }
             if (lane == 0) {
-                const unsigned long long packed =
-                    ((unsigned long long)ordered_key(mk) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)mi);
-                atomicMax(a.winners + ((size_t)k * a.Bpad * kWinnerSlots + g % kWinnerSlots) * kWinnerStride, packed);
                 const size_t o = ((size_t)k * G + g) * a.Bpad;
                 agent_store(a.p_mc + o, mm);
                 agent_store(a.p_s + o, ms);
                 agent_store(a.p_idx + o, mi);
                 agent_store(a.p_l + o, mk);
+                const unsigned long long packed =
+                    ((unsigned long long)ordered_key(mk) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)mi);
+                agent_store(a.winners + (size_t)k * G + g, packed);
             }
-            wait_vmcnt<0>();
-            int last_all = 0;
-            if (lane == 0) last_all = arrive(a, k) ? 1 : 0;
-            if (__shfl(last_all, 0) && lane < kBarrierGroups)
-                agent_store(a.release + kCounterStride * lane, (uint32_t)(k + 1));
         }
     }
 }
@@ -1400,14 +1445,16 @@ int resident_max_coresident(bool gated, bool store) {
     return per_cu * device_cu_count();
 }
 
-bool resident_supported(int B, int r, bool sample, int V, int G) {
-    return B == 1 && r == kResR && !sample && G >= 1 && (int64_t)V <= (int64_t)kResWaves * 64 * G;
+// The slot words of K + 1 positions live in the winner array ([K][Bpad][kWinnerSlots] words, kWinnerStride apart).
+bool resident_supported(int B, int K, int r, bool sample, int V, int G, int Bpad) {
+    return B == 1 && r == kResR && !sample && G >= 1 && (int64_t)V <= (int64_t)kResWaves * 64 * G &&
+           (int64_t)(K + 1) * G <= (int64_t)K * Bpad * kWinnerSlots * kWinnerStride;
 }
 
 // Launched like the tiled round (one workgroup per CU, ordinary launch unless `cooperative`).
 hipError_t launch_markov_resident(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st, hipEvent_t ev_begin,
                                   hipEvent_t ev_end) {
-    if (!resident_supported(a.B, a.r, false, a.V, a.G)) return hipErrorInvalidValue;
+    if (!resident_supported(a.B, a.K, a.r, false, a.V, a.G, a.Bpad)) return hipErrorInvalidValue;
     const void* fn = resident_fn(gated, a.logits_out != nullptr);
     if (ev_begin) (void)hipEventRecord(ev_begin, st);
     RoundArgs copy = a;
