@@ -38,6 +38,7 @@ def _noalloc_abi(D, w, mode, seed, T, tokens, logprobs):
 CASES = [  # (workload, B, K, V, r, mode, weight dtype): the full serving round, then smaller ones
     ("serving", None, None, None, None, S.SAMPLE, S.BF16),
     ("serving", 40, 3, 2000, 128, S.SAMPLE, S.BF16),  # the half-block form
+    ("serving", 1, 3, 3000, 256, S.GREEDY, S.BF16),   # one row at r = 256: the resident round
     ("serving", 5, 3, 3000, 64, S.GREEDY, S.BF16),
     ("serving", 3, 2, 1001, 24, S.SAMPLE, S.F32),
 ]
