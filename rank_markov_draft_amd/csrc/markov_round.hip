@@ -1241,10 +1241,6 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
             break;
         }
         const float u_cur = u_next;
-        if (k + 1 < a.K) {
-            const float* ub = a.U + (size_t)(k + 1) * a.u_kstride;  // wave-uniform base, 32-bit lane offset
-            u_next = live ? ub[(uint32_t)v] : 0.f;
-        }
         // the previous position's pick, from the pick wave through LDS
         int pv;
         if (k == 0) {
@@ -1328,6 +1324,11 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
         if (lane == 0)
             last = __hip_atomic_fetch_add(&stepdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
                    (uint32_t)kResWaves * (uint32_t)(k + 1) - 1u;
+        // the next position's base logit, issued after the wait above so that it lands during the hand-over
+        if (k + 1 < a.K) {
+            const float* ub = a.U + (size_t)(k + 1) * a.u_kstride;  // wave-uniform base, 32-bit lane offset
+            u_next = live ? ub[(uint32_t)v] : 0.f;
+        }
         if (__shfl(last, 0)) {
             // the workgroup's last wave: merge the waves in order, then the partials and the slot word.  The lane
             // index is formed here (the W2 rows leave no register to keep one across the loop)
