@@ -271,8 +271,17 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             if (Gres > round_gmax()) Gres = round_gmax();
         }
         const bool resident = resident_supported(B, K, r, sample, V, Gres, ws.Bpad);
-        int G = resident ? Gres : round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
-        if (!resident) {
+        // up to 64 rows at r = 256 (greedy) whose W2 tiles fit the workgroups' registers keep them there
+        int Grm = 0;
+        if (!resident && B <= 64 && r == 256 && !sample && !cf) {
+            Grm = resident_mfma_max_coresident(H != nullptr, logits_out != nullptr);
+            if (Grm > round_gmax()) Grm = round_gmax();
+        }
+        const bool resident_mfma = !resident && !cf && resident_mfma_supported(B, r, sample, V, Grm);
+        int G = resident ? Gres
+                : resident_mfma ? Grm
+                                : round_max_coresident(r, sample, H != nullptr, round_row_form(B), logits_out != nullptr);
+        if (!resident && !resident_mfma) {
             if (G > round_gmax()) G = round_gmax();
             if (G > ntiles) G = ntiles;
         }
@@ -313,8 +322,10 @@ int markov_draft_impl(const float* U, const void* W1, const void* W2, int wdtype
             a.p_l = ws.p_l;
             a.logits_out = logits_out;
             const bool coop = g_cooperative.load(std::memory_order_relaxed) != 0;
-            hipError_t e = resident ? launch_markov_resident(a, H != nullptr, coop, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)
-                                    : launch_markov_round(a, sample, H != nullptr, coop, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+            hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+            hipError_t e = resident        ? launch_markov_resident(a, H != nullptr, coop, st, e0, e1)
+                           : resident_mfma ? launch_markov_resident_mfma(a, H != nullptr, coop, st, e0, e1)
+                                           : launch_markov_round(a, sample, H != nullptr, coop, st, e0, e1);
             if (e != hipSuccess) return device_fail(e, "draft round launch");
             if (kernel_launches) *kernel_launches = 1;
             return DSPARK_OK;

@@ -155,6 +155,13 @@ int resident_max_coresident(bool gated, bool store);
 bool resident_supported(int B, int K, int r, bool sample, int V, int G, int Bpad);
 hipError_t launch_markov_resident(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st, hipEvent_t ev_begin,
                                   hipEvent_t ev_end);
+// The matrix-core resident round: at most 64 rows, r = 256, greedy, at most 16 vocabulary tiles per workgroup;
+// each workgroup keeps its W2 tiles in registers as matrix-core operands for the whole round.  Same arguments and
+// workspace as the tiled round; no confidence head.
+int resident_mfma_max_coresident(bool gated, bool store);
+bool resident_mfma_supported(int B, int r, bool sample, int V, int G);
+hipError_t launch_markov_resident_mfma(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st,
+                                       hipEvent_t ev_begin, hipEvent_t ev_end);
 
 int mfma_supported_r(int r);
 hipError_t launch_markov_step_mfma(const StepArgs& a, int mode, bool gated, bool vec_u, int G, hipStream_t st);

@@ -1367,6 +1367,328 @@ __global__ void __launch_bounds__(kResThreads, 1) markov_resident_kernel(RoundAr
     }
 }
 
+// ====================================================================================================================
+// The matrix-core resident round: at most 64 rows, r = 256, greedy picks, at most 16 vocabulary tiles per
+// workgroup (V <= 512 G: 131,072 at 256 CUs), gated or not (the gated workload: B = 64, V = 129,280).
+//
+// The tiled round streams W2 at every position and stalls at each grid boundary once its ring and registers
+// are full.  Here a workgroup's W2 tiles stay in registers for the whole round: eight waves, two per SIMD
+// with 256 registers each, each hold the A operands of two 32-id tiles (16 x 8 bf16 per lane and tile, 128
+// registers; rows placed by the same slot order as the tiled round, so a lane's accumulator holds 16
+// consecutive ids).  Per position only the base logits stream, straight into the accumulators (C operand),
+// requested one position ahead as soon as each accumulator's epilogue is done.  X (64 rows, bf16) and the
+// next position's gate rows (fp32, loaded with direct global-to-LDS loads) live in LDS; the B operands are read
+// from X.  The same v_mfma_f32_32x32x16_bf16 with the same operands as the tiled round, seeded with U, gives
+// the same logits.  The end of a position merges the rows over the eight waves in wave order; wave 0 then
+// makes the tiled round's pick atomics, partials and arrival, and wave 1 merges the previous position's row
+// of this workgroup's (rows g < B) while wave 0 waits for the release.
+constexpr int kRmWaves = 4;               // one per SIMD: 512 registers each
+constexpr int kRmThreads = 64 * kRmWaves;
+constexpr int kRmRows = 64;
+constexpr int kRmTiles = 16;              // tiles per workgroup and round
+constexpr int kRmTpw = kRmTiles / kRmWaves;  // tiles per wave
+constexpr int kRmRpw = kRmRows / kRmWaves;   // X rows gathered per wave
+constexpr int kRmXPitch = 2 * kResR + 16;  // bytes per X row in LDS (a 16-byte shift per row: no bank conflicts)
+constexpr int kRmHPitch = 4 * kResR + 16;  // bytes per gate row in LDS
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The tile row held in slot s (the inverse of w2_slot): slot 8a + 4b + c holds row 16b + 4a + c.
+__device__ __forceinline__ int w2_row_of_slot(int s) { return 16 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3); }
+
+template <bool GATED, bool STORE>
+__global__ void __launch_bounds__(kRmThreads, 1) markov_resident_mfma_kernel(RoundArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kRmRows * kRmXPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t hs[GATED ? kRmRows * kRmHPitch : 16];
+    __shared__ float mkey[kRmWaves][kRmRows], mlog[kRmWaves][kRmRows], mmc[kRmWaves][kRmRows], msum[kRmWaves][kRmRows];
+    __shared__ int mid[kRmWaves][kRmRows];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5;
+    const int rho = lane & 31;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int nrb = (a.B + 31) / 32;
+    const int ntw = (a.ntiles - g + G - 1) / G;
+    const float c = a.c;
+    const uint32_t spin_limit = a.spin_limit;
+    const uint64_t tag = launch_tag(a, agent_load(a.epoch));
+    if (g == 0 && wave == 0) {
+        // this launch's pick words and counters, then its tag (read by every workgroup before its first arrival)
+        const size_t nw = (size_t)a.K * a.Bpad * kWinnerSlots;
+        for (size_t i = lane; i < nw; i += 64) agent_store(a.winners + i * kWinnerStride, 0ull);
+        if (lane < kBarrierGroups) {
+            agent_store(a.barrier + kCounterStride * lane, 0u);
+            agent_store(a.release + kCounterStride * lane, 0u);
+        }
+        if (lane == 0) {
+            agent_store(a.top, 0u);
+            agent_store(a.error, 0u);
+        }
+        wait_vmcnt<0>();
+        if (lane == 0) agent_store(a.flag, tag);
+    }
+
+    // W2 tiles (slots wave, wave + kRmWaves, ... of this workgroup's tiles g, g + G, ...) as A operands
+    bf16x8_t wa[kRmTpw][16];
+#pragma unroll
+    for (int tt = 0; tt < kRmTpw; ++tt) {
+        const int j = wave + kRmWaves * tt;
+        const int v = min(32 * (g + G * j) + w2_row_of_slot(rho), a.V - 1);
+        const bf16x8_t* wp = reinterpret_cast<const bf16x8_t*>(a.W2t + (size_t)v * kResR + 8 * half);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) wa[tt][q] = j < ntw ? wp[2 * q] : bf16x8_t{};
+    }
+    // base logits of (position k, tile slot j, row block rb) in the accumulator layout: row 32 rb + rho, ids
+    // 32 t + 16 half .. + 15 (a tail tile's ids past the vocabulary read as 0 and are masked at the epilogue)
+    auto load_u = [&](int k, int j, int rb, f32x16_t& dst) {
+        const int b = min(32 * rb + rho, a.B - 1);
+        const int col = 32 * (g + G * j) + 16 * half;
+        const float* up = a.U + (size_t)k * a.u_kstride + (size_t)b * a.u_stride + col;
+        f32x4_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = col + 4 * i < a.V ? *reinterpret_cast<const f32x4_t*>(up + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dst[4 * i] = q[i].x;
+            dst[4 * i + 1] = q[i].y;
+            dst[4 * i + 2] = q[i].z;
+            dst[4 * i + 3] = q[i].w;
+        }
+    };
+    // the gate rows of position k for this wave's rows, global -> LDS
+    auto load_h = [&](int k) {
+        if constexpr (GATED) {
+#pragma unroll
+            for (int i = 0; i < kRmRpw; ++i) {
+                const int b = kRmRpw * wave + i;
+                if (b < a.B)
+                    __builtin_amdgcn_global_load_lds(
+                        reinterpret_cast<const void*>(a.H + ((size_t)b * a.K + k) * kResR + 4 * lane),
+                        (lds_void_t*)(hs + b * kRmHPitch), 16, 0, 0);
+            }
+        }
+    };
+    // X rows of position k (predecessors from the pick words of k - 1, or the anchors), this wave's rows: lane l
+    // takes row kRmRpw wave + l / kLpr, kCpl consecutive 16-byte chunks
+    constexpr int kLpr = 64 / kRmRpw;       // lanes per row
+    constexpr int kCpl = 32 / kLpr;         // chunks per lane (32 chunks of 16 bytes per row)
+    auto gather = [&](int k) {
+        const int b = kRmRpw * wave + lane / kLpr;
+        const bool vb = b < a.B;
+        int pv = 0;
+        if (vb) {
+            if (k == 0) {
+                pv = a.anchor[b];
+            } else {
+                const unsigned long long wv = pick_word(a, k - 1, b);
+                pv = (int)(0xFFFFFFFFu - (uint32_t)(wv & 0xFFFFFFFFull));
+            }
+            pv = min(max(pv, 0), a.V - 1);
+        }
+        const u32x4_t* wrow = reinterpret_cast<const u32x4_t*>(a.W1 + (size_t)pv * kResR);
+        u32x4_t raw[kCpl];
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) raw[i] = wrow[kCpl * (lane % kLpr) + i];
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) {
+            const int ch = kCpl * (lane % kLpr) + i;
+            u32x4_t o = raw[i];
+            if constexpr (GATED) {
+                const float* hl = reinterpret_cast<const float*>(hs + (vb ? b : 0) * kRmHPitch) + 8 * ch;
+                const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(hl);
+                const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(hl + 4);
+                const float hf[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                const uint32_t w32[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+                uint32_t o32[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_to_f32((uint16_t)(w32[e] & 0xFFFFu)) * hf[2 * e];
+                    const float hi = bf16_to_f32((uint16_t)(w32[e] >> 16)) * hf[2 * e + 1];
+                    o32[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                }
+                o = u32x4_t{o32[0], o32[1], o32[2], o32[3]};
+            }
+            if (!vb) o = u32x4_t{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4_t*>(xs + b * kRmXPitch + 16 * ch) = o;
+        }
+    };
+
+    f32x16_t acc[kRmTpw][2];
+#pragma unroll
+    for (int tt = 0; tt < kRmTpw; ++tt)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            if (wave + kRmWaves * tt < ntw && rb < nrb) load_u(0, wave + kRmWaves * tt, rb, acc[tt][rb]);
+    load_h(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    gather(0);
+    __syncthreads();
+
+    for (int k = 0; k < a.K; ++k) {
+        // per row block: running max and sum of the log-sum-exp, best logit and its slot / tile
+        float m[2] = {kNegBig, kNegBig}, s[2] = {0.f, 0.f}, bl[2] = {-INFINITY, -INFINITY};
+        int bslot[2] = {0, 0}, btile[2] = {-1, -1};
+#pragma unroll
+        for (int tt = 0; tt < kRmTpw; ++tt) {
+            const int j = wave + kRmWaves * tt;
+            if (j >= ntw) continue;
+            const int t = g + G * j;
+            // both row blocks of the tile at once: two independent accumulation chains on the same A operands, so
+            // each MFMA issues while the other chain's previous one completes (rows past the batch read zero X)
+            {
+                const uint8_t* x0 = xs + rho * kRmXPitch + 16 * half;
+                const uint8_t* x1 = x0 + 32 * kRmXPitch;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    acc[tt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[tt][q], *reinterpret_cast<const bf16x8_t*>(x0 + 32 * q), acc[tt][0], 0, 0, 0);
+                    acc[tt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[tt][q], *reinterpret_cast<const bf16x8_t*>(x1 + 32 * q), acc[tt][1], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (rb >= nrb) continue;
+                f32x16_t& lv = acc[tt][rb];
+                const int b = 32 * rb + rho;
+                const int v0 = 32 * t + 16 * half;
+                if constexpr (STORE) {
+                    if (b < a.B) {
+                        float* d = a.logits_out + ((size_t)b * a.K + k) * (size_t)a.V + v0;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (v0 + i < a.V) d[i] = lv[i];
+                    }
+                }
+                // greedy epilogue (ids past the vocabulary masked), as in the tiled round
+                if (v0 + 16 > a.V) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (v0 + i >= a.V) lv[i] = -INFINITY;
+                }
+                float cm = lv[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) cm = fmaxf(cm, lv[i]);
+                const float mn = fmaxf(m[rb], cm);
+                s[rb] *= fast_exp2((m[rb] - mn) * c);
+                m[rb] = mn;
+                const float mc = mn * c;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[rb] += fast_exp2(fmaf(lv[i], c, -mc));
+                if (cm > bl[rb]) {
+                    int sl = 15;
+#pragma unroll
+                    for (int i = 14; i >= 0; --i) sl = (lv[i] == cm) ? i : sl;
+                    bl[rb] = cm;
+                    bslot[rb] = sl;
+                    btile[rb] = t;
+                }
+                // the accumulator is free: the next position's base logits go into it now
+                if (k + 1 < a.K) load_u(k + 1, j, rb, acc[tt][rb]);
+            }
+        }
+        if (k + 1 < a.K) load_h(k + 1);  // every wave has read the gate rows of k (barrier after the gather)
+        // this wave's per-row results: the two lanes of a row merged, then into LDS
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            if (rb >= nrb) continue;
+            int bi = btile[rb] >= 0 ? 32 * btile[rb] + 16 * half + bslot[rb] : 0x7FFFFFFF;
+            float key = bl[rb];
+            float mc2 = m[rb] * c, s2 = s[rb];
+            const float okey = __shfl_xor(key, 32);
+            const int oi = __shfl_xor(bi, 32);
+            const float omc = __shfl_xor(mc2, 32);
+            const float os = __shfl_xor(s2, 32);
+            if (beats(okey, oi, key, bi)) {
+                key = okey;
+                bi = oi;
+            }
+            lse_merge(mc2, s2, omc, os);
+            if (half == 0) {
+                mkey[wave][32 * rb + rho] = key;
+                mid[wave][32 * rb + rho] = bi;
+                mmc[wave][32 * rb + rho] = mc2;
+                msum[wave][32 * rb + rho] = s2;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // one lane per row: the eight waves' results in wave order, then the global pick and partials
+            const int b = lane;
+            if (b < a.B) {
+                float key = mkey[0][b], mc2 = mmc[0][b], s2 = msum[0][b];
+                int bi = mid[0][b];
+#pragma unroll
+                for (int w = 1; w < kRmWaves; ++w) {
+                    const float ok = mkey[w][b];
+                    const int oi = mid[w][b];
+                    if (beats(ok, oi, key, bi)) {
+                        key = ok;
+                        bi = oi;
+                    }
+                    lse_merge(mc2, s2, mmc[w][b], msum[w][b]);
+                }
+                if (k == 0) wait_cleared(a, tag);
+                const unsigned long long packed =
+                    ((unsigned long long)ordered_key(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
+                atomicMax(a.winners + (((size_t)k * a.Bpad + b) * kWinnerSlots + g % kWinnerSlots) * kWinnerStride, packed);
+                const size_t o = ((size_t)k * G + g) * a.Bpad + b;
+                agent_store(a.p_mc + o, mc2);
+                agent_store(a.p_s + o, s2);
+                agent_store(a.p_idx + o, bi);
+                agent_store(a.p_l + o, key);
+            }
+            wait_vmcnt<0>();
+            int last_all = 0;
+            if (lane == 0) last_all = arrive(a, k) ? 1 : 0;
+            if (__shfl(last_all, 0) && lane < kBarrierGroups)
+                agent_store(a.release + kCounterStride * lane, (uint32_t)(k + 1));
+            // the release of position k (the last one's is awaited after the loop)
+            if (k + 1 < a.K) {
+                uint32_t spins = 0;
+                while (released_position(a) < (uint32_t)(k + 1)) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > spin_limit) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+        } else if (wave == 1 && k >= 1 && g < a.B) {
+            finalize_pair(a, g, k - 1, false);  // released before this position began
+        }
+        if (k + 1 < a.K) {
+            wait_vmcnt<0>();  // this wave's gate rows in LDS (and its base logits in registers)
+            __syncthreads();
+            gather(k + 1);
+            __syncthreads();
+        }
+    }
+    // after the last position: its release, then this workgroup's row of it
+    bool timed_out = false;
+    if (wave == 1 && g < a.B) {
+        uint32_t spins = 0;
+        while (released_position(a) < (uint32_t)a.K) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > spin_limit) {
+                timed_out = true;
+                break;
+            }
+        }
+        if (timed_out && lane == 0) agent_store(a.error, 1u);
+        finalize_pair(a, g, a.K - 1, timed_out);
+    }
+    // every workgroup has arrived after its last position, so all have read the epoch: advance it
+    if (g == 0 && wave == 0) {
+        uint32_t spins = 0;
+        while (released_position(a) < (uint32_t)a.K) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > spin_limit) break;
+        }
+        if (lane == 0) agent_store(a.epoch, agent_load(a.epoch) + 1u);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_confidence(const ConfArgs& c, int B, hipStream_t st) {
@@ -1450,6 +1772,38 @@ int resident_max_coresident(bool gated, bool store) {
 bool resident_supported(int B, int K, int r, bool sample, int V, int G, int Bpad) {
     return B == 1 && r == kResR && !sample && G >= 1 && (int64_t)V <= (int64_t)kResWaves * 64 * G &&
            (int64_t)(K + 1) * G <= (int64_t)K * Bpad * kWinnerSlots * kWinnerStride;
+}
+
+static const void* resident_mfma_fn(bool gated, bool store) {
+    return gated ? (store ? reinterpret_cast<const void*>(&markov_resident_mfma_kernel<true, true>)
+                          : reinterpret_cast<const void*>(&markov_resident_mfma_kernel<true, false>))
+                 : (store ? reinterpret_cast<const void*>(&markov_resident_mfma_kernel<false, true>)
+                          : reinterpret_cast<const void*>(&markov_resident_mfma_kernel<false, false>));
+}
+
+int resident_mfma_max_coresident(bool gated, bool store) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_mfma_fn(gated, store), kRmThreads, 0) != hipSuccess)
+        return 0;
+    return per_cu * device_cu_count();
+}
+
+bool resident_mfma_supported(int B, int r, bool sample, int V, int G) {
+    const int64_t ntiles = ((int64_t)V + 31) / 32;
+    return B >= 1 && B <= kRmRows && r == kResR && !sample && G >= 1 && (ntiles + G - 1) / G <= kRmTiles;
+}
+
+hipError_t launch_markov_resident_mfma(const RoundArgs& a, bool gated, bool cooperative, hipStream_t st,
+                                       hipEvent_t ev_begin, hipEvent_t ev_end) {
+    if (!resident_mfma_supported(a.B, a.r, false, a.V, a.G) || a.cf.h) return hipErrorInvalidValue;
+    const void* fn = resident_mfma_fn(gated, a.logits_out != nullptr);
+    if (ev_begin) (void)hipEventRecord(ev_begin, st);
+    RoundArgs copy = a;
+    void* args[] = {&copy};
+    const hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kRmThreads), args, 0, st)
+                                     : hipLaunchKernel(fn, dim3(a.G), dim3(kRmThreads), args, 0, st);
+    if (ev_end) (void)hipEventRecord(ev_end, st);
+    return e;
 }
 
 // Launched like the tiled round (one workgroup per CU, ordinary launch unless `cooperative`).
