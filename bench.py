@@ -443,9 +443,14 @@ def main():
         gated_round()
         gms_, _ = timed_rounds(gated_round, 10)
         gb = w.K * markov_bytes_per_position(w.B, w.V, w.r, gated=True) + 2 * w.B * w.K * w.D + 2 * w.D * w.r + 4 * w.B * w.K * w.r
+        # the gated round keeps W2 on chip (matrix-core resident round): also held to W2 read once per round
+        gcomp = gb - (w.K - 1) * 2 * w.r * w.V
         extras["gated"] = {"round_ms": round(float(gms_.mean()), 4),
                            "tokens_per_s": round(w.B * w.K / (gms_.mean() / 1e3), 1), "bytes_per_round": gb,
-                           "pct_of_hbm_roofline": round(100.0 * gb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gms_.mean()), 2)}
+                           "pct_of_hbm_roofline": round(100.0 * gb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gms_.mean()), 2),
+                           "kernel": "gate GEMM + matrix-core resident round (W2 read once per round)",
+                           "compulsory_bytes_per_round": gcomp,
+                           "pct_of_compulsory_roofline": round(100.0 * gcomp / (HBM_PEAK_GBS * 1e9) * 1e3 / float(gms_.mean()), 2)}
 
         # its top-16 Selector form: the gate GEMM, then top-16, the gated pair tables and the walk
         gsws = torch.empty(D.dspark_selector_workspace_bytes(w.B, w.K, w.V, w.r, 16), dtype=torch.uint8, device=dev)
