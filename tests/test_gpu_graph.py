@@ -38,8 +38,10 @@ def _replays_match(run, outputs, n=4):
         _ = (torch.randn(4096, device=outputs[0].device) * i).sum().item()  # eager work between replays
 
 
-@pytest.mark.parametrize("shape", [(128, 4, 4096, 256, S.BF16), (8, 3, 1002, 64, S.BF16), (3, 3, 300, 24, S.F32)],
-                         ids=["whole-round", "per-position-V%4", "per-position-fp32"])
+@pytest.mark.parametrize("shape", [(128, 4, 4096, 256, S.BF16), (8, 3, 1002, 64, S.BF16), (3, 3, 300, 24, S.F32),
+                                   (1, 4, 3000, 256, S.BF16), (16, 4, 3000, 256, S.BF16)],
+                         ids=["whole-round", "per-position-V%4", "per-position-fp32", "one-row-r256",
+                              "16-rows-r256"])
 @pytest.mark.parametrize("mode", [S.GREEDY, S.SAMPLE], ids=["greedy", "sample"])
 def test_markov_draft_graph(D, shape, mode):
     B, K, V, r, wd = shape

@@ -320,12 +320,13 @@ def test_cooperative_launch_matches_default(D):
     assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
 
 
-@pytest.mark.parametrize("B,r", [(16, 64), (1, 256)], ids=["tiled", "resident"])
+@pytest.mark.parametrize("B,r", [(16, 64), (1, 256), (16, 256)], ids=["tiled", "resident", "resident-mfma"])
 def test_device_timeout_is_reported(D, B, r):
-    """Failure path of the whole-round kernels (the tiled round, and the resident round of a single row at
-    r = 256), forced from the host: a spin limit of one sleep makes their bounded waits give up (every wait still
-    ends, so the kernel exits normally).  The status call then reports DSPARK_EDEVICE; with the default limit
-    restored the same workspace drafts correctly and reports OK."""
+    """Failure path of the whole-round kernels (the tiled round, the resident round of a single row at r = 256,
+    and the matrix-core resident round of up to 64 rows at r = 256), forced from the host: a spin limit of one
+    sleep makes their bounded waits give up (every wait still ends, so the kernel exits normally).  The status
+    call then reports DSPARK_EDEVICE; with the default limit restored the same workspace drafts correctly and
+    reports OK."""
     w = S.workload("serving", B=B, K=3, V=4096, r=r, mode=S.GREEDY)
     args = (t_f32(w.U), t_w(w.W1), t_w(w.W2T), t_i32(w.anchor))
     nbytes = D.dspark_markov_workspace_bytes(w.B, w.K, w.V, w.r, D.DSPARK_BF16, D.DSPARK_W2_VR)

@@ -39,6 +39,7 @@ CASES = [  # (workload, B, K, V, r, mode, weight dtype): the full serving round,
     ("serving", None, None, None, None, S.SAMPLE, S.BF16),
     ("serving", 40, 3, 2000, 128, S.SAMPLE, S.BF16),  # the half-block form
     ("serving", 1, 3, 3000, 256, S.GREEDY, S.BF16),   # one row at r = 256: the resident round
+    ("serving", 16, 3, 3000, 256, S.GREEDY, S.BF16),  # up to 64 rows at r = 256: the matrix-core resident round
     ("serving", 5, 3, 3000, 64, S.GREEDY, S.BF16),
     ("serving", 3, 2, 1001, 24, S.SAMPLE, S.F32),
 ]
