@@ -115,6 +115,10 @@ size_t dspark_markov_workspace_bytes(int B, int K, int V, int r, int wdtype, int
  * mode     DSPARK_GREEDY or DSPARK_SAMPLE; seed and temperature (> 0) are used in SAMPLE mode only.
  * tokens   [B, K] int32 output.   logprobs: [B, K] fp32 output or NULL.
  * Accumulation is fp32 over bf16 (or fp32) products; the gated bf16 path rounds x to bf16 (nearest even).
+ * Greedy bf16 drafts at r = 256 with a [V, r] W2 keep W2 on chip for the whole round when it fits: one row with
+ * V <= 640 x (CU count) (each lane holds one W2 row; dot products summed in two fixed-order halves), and 2 .. 64
+ * rows with V <= 512 x (CU count) and no confidence head (each workgroup holds its W2 tiles as matrix-core
+ * operands; the same per-tile contraction as the tiled round, rows merged over waves in a fixed order).
  * Device-side failure: the whole-round kernel (one persistent launch per call) waits on other workgroups with
  * bounded spins.  If a wait gives up (it never should on an idle device; a device shared with other work that
  * keeps workgroups from being co-resident could cause it), the kernel still exits normally, writes tokens = -1
