@@ -1098,15 +1098,16 @@ __global__ void __launch_bounds__(64) confidence_kernel(ConfArgs c) {
 //
 // With no stream to overlap, a position is a chain of memory round trips, so the hand-over is kept short: each
 // workgroup writes its packed (key, ~id) word for position k into a slot of its own (slot[k][g] in the winner
-// array, cleared at the start of the launch; a written word is never zero), and wave 0 of every workgroup polls
-// the G slots of position k until all are written and takes their maximum, the same pick the tiled round's atomic
-// maximum gives.  That replaces the atomic maximum, the arrival counters, the release word and the pick read by
-// one store and one polled read.  The log-sum-exp partials are written just before the slot word, and each wave
-// waits for all its stores at the next position before the workgroup's next slot word, so partials of position k
-// are complete once every slot of position k + 1 (or every done word after the last position) is written; the
-// finalizer of workgroup 0 merges them then, one position behind.
+// array, cleared at the start of the launch; a written word is never zero), and an eleventh wave of every
+// workgroup (the pick wave, which holds no W2 row) polls the G slots of position k until all are written and takes
+// their maximum, the same pick the tiled round's atomic maximum gives, then hands it to its workgroup through LDS.
+// That replaces the atomic maximum, the arrival counters, the release word and the pick read by one store and one
+// polled read.  The log-sum-exp partials are written just before the slot word, and each wave waits for all its
+// stores at the next position before the workgroup's next slot word, so partials of position k are complete once
+// every slot of position k + 1 (or every done word after the last position) is written; the pick wave of
+// workgroup 0 merges them then, one position behind.
 constexpr int kResWaves = 10;                       // waves holding W2 rows, one id per lane
-constexpr int kResThreads = 64 * (kResWaves + 1);   // and the finalizer
+constexpr int kResThreads = 64 * (kResWaves + 1);   // and the pick wave
 constexpr int kResR = 256;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -1399,7 +1400,7 @@ template <bool GATED, bool STORE>
 __global__ void __launch_bounds__(kRmThreads, 1) markov_resident_mfma_kernel(RoundArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t xs[kRmRows * kRmXPitch];
     __shared__ __attribute__((aligned(16))) uint8_t hs[GATED ? kRmRows * kRmHPitch : 16];
-    __shared__ float mkey[kRmWaves][kRmRows], mlog[kRmWaves][kRmRows], mmc[kRmWaves][kRmRows], msum[kRmWaves][kRmRows];
+    __shared__ float mkey[kRmWaves][kRmRows], mmc[kRmWaves][kRmRows], msum[kRmWaves][kRmRows];
     __shared__ int mid[kRmWaves][kRmRows];
 
     const int lane = threadIdx.x & 63;
