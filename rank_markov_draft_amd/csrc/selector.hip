@@ -469,7 +469,9 @@ __global__ void __launch_bounds__(256) pair_score_kernel(SelectorArgs a) {
     float* out = a.scores + (size_t)b * (a.topk + (size_t)(a.K - 1) * a.topk * a.topk) +
                  (t == 0 ? 0 : a.topk + (size_t)(t - 1) * a.topk * a.topk);
     const int ii = threadIdx.x / kPairBlock, jj = threadIdx.x % kPairBlock;
-    for (int j0 = 0; j0 < a.topk; j0 += kPairBlock) {
+    // blocks of 16 candidates dealt over the grid's third dimension (a loop per workgroup made the blocks of
+    // a large top-k one after another: 50 us for three 512 x 512 tables)
+    for (int j0 = blockIdx.z * kPairBlock; j0 < a.topk; j0 += gridDim.z * kPairBlock) {
         const int nj = min(kPairBlock, a.topk - j0);
         __syncthreads();
         if ((int)threadIdx.x < ni) rid[threadIdx.x] = (t == 0) ? a.anchor[b] : cand_p[i0 + threadIdx.x];
@@ -1018,7 +1020,8 @@ hipError_t launch_topk(const float* U, int64_t u_stride, int rows, int V, int to
 int topk_supported(int V, int topk) { return topk >= 1 && topk <= V && (topk <= kRadixMaxK || V <= kSortMax); }
 
 hipError_t launch_pair_scores(const SelectorArgs& a, hipStream_t st) {
-    const dim3 grid(a.B * a.K, (a.topk + kPairBlock - 1) / kPairBlock);
+    const int nb = (a.topk + kPairBlock - 1) / kPairBlock;
+    const dim3 grid(a.B * a.K, nb, nb < 64 ? nb : 64);
     const bool vec = ((uintptr_t)a.A % 16 == 0) && ((uintptr_t)a.Bemb % 16 == 0) && (a.r % (a.bf16 ? 8 : 4) == 0);
     if (a.bf16 && vec && a.r % 16 == 0) {
         if (a.topk <= kPairTile) {
