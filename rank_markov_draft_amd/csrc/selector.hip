@@ -778,6 +778,8 @@ __global__ void __launch_bounds__(64) walk_kernel(SelectorArgs a) {
         const int32_t* cand_t = cands + (size_t)t * a.topk;
         float bk = -INFINITY, bl = 0.f, m = kMinFinite, s = 0.f;
         int bi = 0x7FFFFFFF, bs = 0;
+        // unrolled so that a lane's loads of the row are in flight together (same order per lane)
+#pragma unroll 8
         for (int j = lane; j < a.topk; j += 64) {
             const float l = rowp[j];
             const int cid = cand_t[j];
