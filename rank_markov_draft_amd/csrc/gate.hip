@@ -7,15 +7,21 @@
 //
 // Workgroup = eight waves sharing one 32 x 32 output tile; wave w accumulates the 64-wide k steps
 // [w n / 8, (w + 1) n / 8) of the n = D / 64 steps (split-K inside the workgroup, summed in a fixed order
-// through LDS, so the result is deterministic).  Per k step a wave reads its A fragments (h rows,
-// k-contiguous) straight from global memory and stages the Wg block [64 k x 32 n] transposed through LDS so
-// that B fragments are k-contiguous too.  The next step's loads are issued before the current step's MFMAs.
+// through LDS, so the result is deterministic).  Per k step a wave reads its h block [32 rows x 64 k] with
+// eight lanes per 128-byte row segment (whole cache lines; fragment-shaped loads, 32 bytes from each of 32
+// rows per instruction, made L2 serve quarter lines) and stages it through LDS for the A fragments, and it
+// stages the Wg block [64 k x 32 n] transposed through LDS so that B fragments are k-contiguous too.  The
+// next step's loads are issued before the current step's MFMAs.
 // The product is small (one workgroup per output tile: 256 at 1024 rows x r = 256) and each step waits on
 // memory, so the k range is split eight ways: two waves per SIMD hide each other's waits and each wave's
 // chain is short (at rows = 1024, D = 4096, r = 256, event-timed with launch: 21.7 us with four waves, 17.6
-// with eight, 20.0 with sixteen; four k steps of loads in flight per wave instead of one: 19.5).  What remains
-// is the tiling: the 32 x 32 tiles re-read h once per column block and Wg once per row block, about 128 MB
-// of L2 reads for 10.5 MB of operands.
+// with eight, 20.0 with sixteen; four k steps of loads in flight per wave instead of one: 19.5).  Same-box
+// A/B at that shape: the whole-line h loads 21.3 -> 20.7 us.  Not kept: two k steps of loads in flight (21.4
+// us); the Wg transpose written as 32-bit (k, k + 1) pairs after a swap between lanes l and l ^ 4 (21.4 us;
+// leaving the transpose stores out altogether would save 2.5 us); each workgroup taking its k chunks in a
+// rotated order so that the workgroups sharing h rows or Wg columns do not read the same lines at once
+// (20.7 us).  What remains is the tiling: the 32 x 32 tiles re-read h once per column block and Wg once per
+// row block, about 128 MB of L2 reads for 10.5 MB of operands.
 #include "internal.hpp"
 
 namespace dspark {
@@ -26,19 +32,20 @@ constexpr int kGateWaves = 8;
 constexpr int kGateThreads = 64 * kGateWaves;
 constexpr int kKStep = 64;                   // k per iteration and wave
 constexpr int kBtStride = kKStep + 8;        // bf16 elements per LDS row of the transposed Wg block
+constexpr int kAtStride = kKStep + 8;        // bf16 elements per LDS row of the h block
 
 struct GateLoads {
-    u32x4_t a[4];  // h[row][k0 + 16*kk + 8*half .. +8], kk = 0..3
+    u32x4_t a[4];  // h[row0 + 8*i + lane/8][k0 + 8*(lane%8) .. +8], i = 0..3
     u32x4_t w[4];  // Wg[k0 + krow][n0 + 8*nch .. +8] for chunk c = lane + 64*q
 };
 
 __device__ __forceinline__ void gate_load(GateLoads& L, const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
-                                          int rows, int D, int r, int row, int n0, int k0, int lane) {
-    const int half = lane >> 5;
+                                          int rows, int D, int r, int row0, int n0, int k0, int lane) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        L.a[kk] = (row < rows) ? *reinterpret_cast<const u32x4_t*>(h + (size_t)row * D + k0 + 16 * kk + 8 * half)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 8 * i + (lane >> 3);
+        L.a[i] = (row < rows) ? *reinterpret_cast<const u32x4_t*>(h + (size_t)row * D + k0 + 8 * (lane & 7))
+                              : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -51,20 +58,25 @@ __device__ __forceinline__ void gate_load(GateLoads& L, const uint16_t* __restri
 __global__ void __launch_bounds__(kGateThreads) gate_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
                                                           int rows, int D, int r, float* __restrict__ H) {
     __shared__ __attribute__((aligned(16))) uint16_t bt[kGateWaves][32 * kBtStride];
+    __shared__ __attribute__((aligned(16))) uint16_t at[kGateWaves][32 * kAtStride];
     __shared__ float red[kGateWaves - 1][32 * 32];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
     const int row0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
-    const int row = row0 + (lane & 31);
     const int nsteps = D / kKStep;
     const int kbeg = (wave * nsteps / kGateWaves) * kKStep, kend = ((wave + 1) * nsteps / kGateWaves) * kKStep;
 
     f32x16_t acc = {};
     GateLoads cur, nxt;
-    if (kbeg < kend) gate_load(cur, h, Wg, rows, D, r, row, n0, kbeg, lane);
+    if (kbeg < kend) gate_load(cur, h, Wg, rows, D, r, row0, n0, kbeg, lane);
     uint16_t* my = bt[wave];
+    uint16_t* ma = at[wave];
     for (int k0 = kbeg; k0 < kend; k0 += kKStep) {
-        if (k0 + kKStep < kend) gate_load(nxt, h, Wg, rows, D, r, row, n0, k0 + kKStep, lane);
+        if (k0 + kKStep < kend) gate_load(nxt, h, Wg, rows, D, r, row0, n0, k0 + kKStep, lane);
+        // the h block into LDS as loaded: ma[row][k]
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4_t*>(ma + (8 * i + (lane >> 3)) * kAtStride + 8 * (lane & 7)) = cur.a[i];
         // transpose the Wg block into LDS: my[n][k]
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -81,8 +93,9 @@ __global__ void __launch_bounds__(kGateThreads) gate_kernel(const uint16_t* __re
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(ma + (lane & 31) * kAtStride + 16 * kk + 8 * half);
             const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(my + (lane & 31) * kBtStride + 16 * kk + 8 * half);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.a[kk]), bf, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
         if (k0 + kKStep < kend) cur = nxt;
