@@ -168,16 +168,18 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
     if (VEC) {
         const int nq = V >> 2;
         const f32x4_t* u4 = reinterpret_cast<const f32x4_t*>(u);
-        for (int q0 = 0; q0 < nq; q0 += kTkThreads * kTkUnroll) {
-            f32x4_t x[kTkUnroll];
+        constexpr int kChunk = kTkThreads * kTkUnroll;  // 16-byte units per chunk of the row
+        auto load = [&](int q0, int j) {
+            const int q = q0 + j * kTkThreads + (int)threadIdx.x;
+            return q < nq ? __builtin_nontemporal_load(u4 + q) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        };
+        // Prefilter on values alone: an element can enter the list only if it is >= the threshold value (ties
+        // are then settled by offer's exact order).  After the first few chunks almost no lane of the wave
+        // passes, and one maximum and one ballot cover a load's 4 elements.
+        f32x4_t x[kTkUnroll];
 #pragma unroll
-            for (int j = 0; j < kTkUnroll; ++j) {
-                const int q = q0 + j * kTkThreads + (int)threadIdx.x;
-                x[j] = q < nq ? __builtin_nontemporal_load(u4 + q) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            }
-            // Prefilter on values alone: an element can enter the list only if it is >= the threshold value
-            // (ties are then settled by offer's exact order).  After the first few iterations almost no
-            // lane of the wave passes, and one maximum and one ballot cover the lane's 16 elements.
+        for (int j = 0; j < kTkUnroll; ++j) x[j] = load(0, j);
+        {
             float mj[kTkUnroll];
             float mx = -INFINITY;
 #pragma unroll
@@ -185,28 +187,48 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
                 mj[j] = fmaxf(fmaxf(x[j].x, x[j].y), fmaxf(x[j].z, x[j].w));
                 mx = fmaxf(mx, mj[j]);
             }
-            if (q0 == 0) {
-                // Start the filter at the L-th largest lane maximum of the first chunk: the L lanes at or above
-                // it hold L elements at least that large, so no smaller element can enter the wave's top-L.
-                // Equal values still pass (id bound INT_MAX) and are settled exactly.  Without it every element
-                // of the first chunk is a candidate and the merges of the start dominate the scan.
-                thv = wave_lth_largest<L>(mx);
-                thi = 0x7FFFFFFF;
-            } else if (L > 16 && (q0 / (kTkThreads * kTkUnroll)) % 4 == 0) {
-                adopt_shared();  // pick up the other waves' progress now and then
-            }
-            if (__ballot(mx >= thv)) {
+            // Start the filter at the L-th largest lane maximum of the first chunk: the L lanes at or above it
+            // hold L elements at least that large, so no smaller element can enter the wave's top-L.  Equal
+            // values still pass (id bound INT_MAX) and are settled exactly.  Without it every element of the
+            // first chunk is a candidate and the merges of the start dominate the scan.
+            thv = wave_lth_largest<L>(mx);
+            thi = 0x7FFFFFFF;
 #pragma unroll
-                for (int j = 0; j < kTkUnroll; ++j) {
-                    if (__ballot(mj[j] >= thv)) {
-                        const int q = q0 + j * kTkThreads + (int)threadIdx.x;
-                        const int id = q < nq ? 4 * q : 0x7FFFFFFC;
-                        offer(x[j].x, id);
-                        offer(x[j].y, id + 1);
-                        offer(x[j].z, id + 2);
-                        offer(x[j].w, id + 3);
-                    }
+            for (int j = 0; j < kTkUnroll; ++j) {
+                if (__ballot(mj[j] >= thv)) {
+                    const int q = j * kTkThreads + (int)threadIdx.x;
+                    const int id = q < nq ? 4 * q : 0x7FFFFFFC;
+                    offer(x[j].x, id);
+                    offer(x[j].y, id + 1);
+                    offer(x[j].z, id + 2);
+                    offer(x[j].w, id + 3);
                 }
+            }
+        }
+        // The following chunks: a lane's load j of the next chunk is issued as soon as its load j of this chunk
+        // has been filtered (and its rare candidates offered), so the wave keeps kTkUnroll loads in flight while
+        // it filters (the offers, their order and the thresholds are those of filtering chunk by chunk).  At
+        // 2048 rows of 151936 against issuing each chunk's loads after the previous chunk's filter: k = 16 202
+        // us either way, k = 64 229 -> 225 us; a plain read of the same rows in this access pattern takes 185
+        // us, so the difference to it is not the filter's latency between chunks.  (The offers are written out
+        // here rather than in a helper lambda: a lambda the compiler did not inline kept the captured list and
+        // threshold in scratch memory, and the scan ran 4.7x slower.)
+#pragma unroll
+        for (int j = 0; j < kTkUnroll; ++j) x[j] = load(kChunk, j);
+        for (int q0 = kChunk; q0 < nq; q0 += kChunk) {
+            if (L > 16 && (q0 / kChunk) % 4 == 0) adopt_shared();  // pick up the other waves' progress now and then
+#pragma unroll
+            for (int j = 0; j < kTkUnroll; ++j) {
+                const float m = fmaxf(fmaxf(x[j].x, x[j].y), fmaxf(x[j].z, x[j].w));
+                if (__ballot(m >= thv)) {
+                    const int q = q0 + j * kTkThreads + (int)threadIdx.x;
+                    const int id = q < nq ? 4 * q : 0x7FFFFFFC;
+                    offer(x[j].x, id);
+                    offer(x[j].y, id + 1);
+                    offer(x[j].z, id + 2);
+                    offer(x[j].w, id + 3);
+                }
+                x[j] = load(q0 + kChunk, j);
             }
         }
     } else {
