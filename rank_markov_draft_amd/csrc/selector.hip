@@ -31,7 +31,7 @@ __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
 
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkUnroll = 4;  // independent 16-byte loads in flight per lane (8 waves per SIMD keep ~128 KB per CU in flight)
-constexpr int kTkBuf = 256;                  // candidate slots per wave
+constexpr int kTkBuf = 128;                  // candidate slots per wave (a flush at 64 leaves at most 63 + 64 pending)
 
 // Compare-exchange across the wave: this lane and lane ^ j hold two entries; this lane keeps the better one
 // (under (value desc, id asc)) when keep_better, else the worse one.
@@ -88,7 +88,7 @@ __device__ __forceinline__ float wave_lth_largest(float t) {
 // Top-k (k <= L, L = 16, 32 or 64) of each row, one workgroup per row.  Each wave keeps an exact sorted list of
 // its best 64 entries (lane s holds rank s) and the list's L-th entry as a threshold; every element is compared
 // once against the threshold and the few that beat it are appended to the wave's LDS buffer, which is merged
-// into the list when it fills: each 64-entry chunk of the buffer by a bitonic sort and one bitonic merge (28
+// into the list once it holds 64: each 64-entry chunk of the buffer by a bitonic sort and one bitonic merge (28
 // exchange steps; with L rounds of a six-step wave arg-max instead, 2048 rows of 151936 took 0.22 ms at L = 16
 // and 0.52 ms at L = 64, against 0.20 and 0.23 ms so).
 // The row is streamed with kTkUnroll independent 16-byte loads per lane, so the scan runs at memory speed; the
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu
                 bi[slot] = id;
             }
             cnt += __popcll(msk);
-            if (cnt > kTkBuf - 64) flush();
+            if (cnt >= 64) flush();  // early: each flush tightens the threshold (at 192 pending the scan ran 1-7% longer)
         }
     };
     if (VEC) {
