@@ -387,6 +387,24 @@ def main():
                                     "tokens_per_s": round(w.B * w.K / (sms_.mean() / 1e3), 1),
                                     "bytes_per_round": sb,
                                     "pct_of_hbm_roofline": round(100.0 * sb / (HBM_PEAK_GBS * 1e9) * 1e3 / float(sms_.mean()), 2)}
+        # the practical ceiling of the Selector's dominant stream: the same base logits read once by the plain
+        # streaming kernel (16-byte non-temporal loads, as the top-k reads them), after the same eviction
+        sel_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        sel_pad = torch.zeros(4, dtype=torch.float32, device=dev)
+        u_all = U.view(-1)
+
+        def base_logits_read():
+            D.dspark_stream_read(sel_pad, u_all, sel_sink)
+
+        base_logits_read()
+        urd, _ = timed_rounds(base_logits_read, 10)
+        u_bytes = u_all.numel() * u_all.element_size()
+        extras["selector_top16"]["base_logits_read"] = {
+            "what": "the Selector's base logits read once by a plain streaming kernel, evicted like a round",
+            "ms": round(float(urd.mean()), 4), "bytes": u_bytes,
+            "GB_per_s": round(u_bytes / (float(urd.mean()) * 1e-3) / 1e9, 1),
+            "selector_round_fraction": round(float(urd.mean()) / float(sms_.mean()), 3)}
+        del u_all
 
         # top-k sweep: the Selector execution of the Markov rule (W1 = A, W2 = Bemb^T) restricted to the
         # top-k candidates, against the full-vocabulary greedy head on the same inputs: token agreement (and the
