@@ -450,12 +450,13 @@ def main():
         h, Wg = to_w(w.h), to_w(w.Wg)
         anc = torch.from_numpy(w.anchor).to(dev)
         Hbuf = torch.empty((w.B, w.K, w.r), dtype=torch.float32, device=dev)
+        gws = torch.empty(max(D.dspark_gate_workspace_bytes(w.B * w.K, w.D, w.r), 1), dtype=torch.uint8, device=dev)
         tok_g = torch.empty((w.B, w.K), dtype=torch.int32, device=dev)
         lp_g = torch.empty((w.B, w.K), dtype=torch.float32, device=dev)
         gws = torch.empty(D.dspark_markov_workspace_bytes(w.B, w.K, w.V, w.r, 1, 1), dtype=torch.uint8, device=dev)
 
         def gated_round():
-            D.dspark_gate(h, Wg, out=Hbuf)
+            D.dspark_gate(h, Wg, out=Hbuf, workspace=gws)
             D.dspark_markov_draft(U, W1g, W2g, anc, H=Hbuf, tokens=tok_g, logprobs=lp_g, workspace=gws)
 
         gated_round()
@@ -474,7 +475,7 @@ def main():
         gsws = torch.empty(D.dspark_selector_workspace_bytes(w.B, w.K, w.V, w.r, 16), dtype=torch.uint8, device=dev)
 
         def gated_sel_round():
-            D.dspark_gate(h, Wg, out=Hbuf)
+            D.dspark_gate(h, Wg, out=Hbuf, workspace=gws)
             D.dspark_selector_draft(U, W1g, W2g, anc, H=Hbuf, topk=16, workspace=gsws)
 
         gated_sel_round()

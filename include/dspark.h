@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 
 /* status codes */
 #define DSPARK_OK 0
@@ -262,8 +262,18 @@ int dspark_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_by
  * no formula; this library takes a bias-free linear map followed by the logistic sigmoid.
  * h [rows, D] bf16, Wg [D, r] bf16, H [rows, r] fp32 output.  fp32 accumulation.
  * D % 256 == 0 and r % 32 == 0 are required (DSPARK_EUNSUPPORTED otherwise).
+ * workspace (device, 16-byte aligned, owned by the caller, contents need not be initialised) may be NULL.  With
+ * at least dspark_gate_workspace_bytes(rows, D, r) bytes (a non-zero size) and a 16-byte aligned H, the
+ * product runs split over the k range in two launches (partial sums in the workspace, then their fixed-order
+ * sum and the sigmoid); otherwise, or with a NULL workspace, in one launch.  Both are deterministic; their
+ * results may differ in the last bits (another summation order).  A workspace smaller than that size, or
+ * misaligned, is DSPARK_EINVAL.  Calls sharing one workspace must not overlap.
  */
-int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* stream);
+int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace bytes of dspark_gate's split-k form for these sizes (0: it does not apply; pass NULL). */
+size_t dspark_gate_workspace_bytes(int rows, int D, int r);
 
 /* ------------------------------------------------------------------------------------------------ */
 /* Selector-style top-k truncation                                                                  */

@@ -60,7 +60,8 @@ def _load_lib():
         "dspark_markov_logits": ([vp, i64, vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, sz, vp], i32),
         "dspark_pack_w2": ([vp, i32, i32, i32, vp, vp], i32),
         "dspark_stream_read": ([vp, sz, vp, sz, vp, vp], i32),
-        "dspark_gate": ([vp, vp, i32, i32, i32, vp, vp], i32),
+        "dspark_gate": ([vp, vp, i32, i32, i32, vp, vp, sz, vp], i32),
+        "dspark_gate_workspace_bytes": ([i32, i32, i32], sz),
         "dspark_topk_workspace_bytes": ([i32, i32, i32], sz),
         "dspark_topk": ([vp, i64, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "dspark_selector_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
@@ -352,8 +353,13 @@ def dspark_stream_read(a, b, sink, *, stream=None):
                                        _stream(stream)), "dspark_stream_read")
 
 
-def dspark_gate(h, Wg, *, out=None, stream=None):
-    """H = sigmoid(h Wg): h [..., D] bf16, Wg [D, r] bf16 -> [..., r] fp32."""
+def dspark_gate_workspace_bytes(rows: int, D: int, r: int) -> int:
+    return int(_lib.dspark_gate_workspace_bytes(rows, D, r))
+
+
+def dspark_gate(h, Wg, *, out=None, workspace=None, split_k=True, stream=None):
+    """H = sigmoid(h Wg): h [..., D] bf16, Wg [D, r] bf16 -> [..., r] fp32.  split_k=False (or sizes the split
+    form does not take) runs the single-launch form without a workspace."""
     with _on(stream):
         _dev(h, "h", torch.bfloat16)
         _dev(Wg, "Wg", torch.bfloat16, 2)
@@ -363,7 +369,9 @@ def dspark_gate(h, Wg, *, out=None, stream=None):
         rows = h.numel() // D
         if out is None:
             out = torch.empty(tuple(h.shape[:-1]) + (r,), dtype=torch.float32, device=h.device)
-        _check(_lib.dspark_gate(_p(h), _p(Wg), rows, D, r, _p(out), _stream(stream)), "dspark_gate")
+        nbytes = int(_lib.dspark_gate_workspace_bytes(rows, D, r)) if split_k else 0
+        ws, wsb = (_workspace(nbytes, h.device, workspace) if nbytes > 0 else (None, 0))
+        _check(_lib.dspark_gate(_p(h), _p(Wg), rows, D, r, _p(out), _p(ws), wsb, _stream(stream)), "dspark_gate")
         return out
 
 

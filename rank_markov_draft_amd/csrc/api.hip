@@ -640,7 +640,13 @@ int dspark_markov_logits(const float* U_k, int64_t u_stride, const void* W1, con
                     nullptr, nullptr, nullptr, 1, nullptr, out, st);
 }
 
-int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* stream) {
+size_t dspark_gate_workspace_bytes(int rows, int D, int r) {
+    if (rows <= 0 || D <= 0 || r <= 0 || D % 256 != 0 || r % 32 != 0) return 0;
+    return gate_splitk_bytes(rows, D, r);
+}
+
+int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H, void* workspace, size_t workspace_bytes,
+                void* stream) {
     g_err[0] = 0;
     if (!h || !Wg || !H) return fail(DSPARK_EINVAL, "NULL buffer");
     if (rows <= 0 || D <= 0 || r <= 0) return fail(DSPARK_EINVAL, "rows, D and r must be positive");
@@ -648,7 +654,12 @@ int dspark_gate(const void* h, const void* Wg, int rows, int D, int r, float* H,
         return fail(DSPARK_EUNSUPPORTED, "gate needs D %% 256 == 0 and r %% 32 == 0 (D=%d r=%d)", D, r);
     if (!aligned16(h) || !aligned16(Wg)) return fail(DSPARK_EINVAL, "h and Wg must be 16-byte aligned");
     if (rows > 65535 * 32) return fail(DSPARK_EUNSUPPORTED, "too many rows");
-    hipError_t e = launch_gate((const uint16_t*)h, (const uint16_t*)Wg, rows, D, r, H, (hipStream_t)stream);
+    if (workspace && workspace_bytes < dspark_gate_workspace_bytes(rows, D, r))
+        return fail(DSPARK_EINVAL, "gate workspace too small (%zu < %zu bytes)", workspace_bytes,
+                    dspark_gate_workspace_bytes(rows, D, r));
+    if (workspace && !aligned16(workspace)) return fail(DSPARK_EINVAL, "workspace must be 16-byte aligned");
+    hipError_t e = launch_gate((const uint16_t*)h, (const uint16_t*)Wg, rows, D, r, H, workspace, workspace_bytes,
+                               (hipStream_t)stream);
     if (e != hipSuccess) return device_fail(e, "gate launch");
     return DSPARK_OK;
 }

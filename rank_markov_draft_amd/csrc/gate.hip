@@ -22,6 +22,8 @@
 // rotated order so that the workgroups sharing h rows or Wg columns do not read the same lines at once
 // (20.7 us).  What remains is the tiling: the 32 x 32 tiles re-read h once per column block and Wg once per
 // row block, about 128 MB of L2 reads for 10.5 MB of operands.
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace dspark {
@@ -119,9 +121,134 @@ __global__ void __launch_bounds__(kGateThreads) gate_kernel(const uint16_t* __re
     }
 }
 
+// Split-K form (a workspace is given): 64 x 64 output tiles, so h is re-read once per 64 columns and Wg once
+// per 64 rows (half the reads of the 32 x 32 tiles), with the k range split over kSkSplits workgroups per tile to
+// keep 256 workgroups at 1024 rows x r = 256.  Eight waves: four 32 x 32 sub-tiles x two halves of the
+// workgroup's k slice.  Per 64-wide k step the 256 threads of a k half stage its h block [64 rows x 64 k] and
+// Wg block [64 k x 64 n] (transposed to [n][k]) once into a double-buffered LDS stage that its four waves read.
+// The two halves are summed in LDS (half 0 + half 1) and each workgroup writes its slice's partial sums; a
+// second kernel adds the slices in order (((p0 + p1) + p2) + p3) and applies the sigmoid, so the result is
+// deterministic.
+constexpr int kSkSplits = 4;
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = 64 * kSkWaves;
+
+struct SkLoads {
+    u32x4_t h[2];  // chunk c = t + 256 i: h[row0 + c / 8][k0 + 8 (c % 8) .. +8]
+    u32x4_t w[2];  // chunk c = t + 256 i: Wg[k0 + c / 8][n0 + 8 (c % 8) .. +8]
+};
+
+__device__ __forceinline__ void sk_load(SkLoads& L, const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
+                                        int rows, int D, int r, int row0, int n0, int k0, int t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = t + 256 * i;
+        const int row = row0 + (c >> 3);
+        L.h[i] = row < rows ? *reinterpret_cast<const u32x4_t*>(h + (size_t)row * D + k0 + 8 * (c & 7))
+                            : u32x4_t{0u, 0u, 0u, 0u};
+        L.w[i] = *reinterpret_cast<const u32x4_t*>(Wg + (size_t)(k0 + (c >> 3)) * r + n0 + 8 * (c & 7));
+    }
+}
+
+__device__ __forceinline__ void sk_store(const SkLoads& L, uint16_t* __restrict__ hb, uint16_t* __restrict__ wb, int t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = t + 256 * i;
+        const int row = c >> 3, ch = c & 7;  // h: row, k chunk; Wg: k-row, n chunk
+        *reinterpret_cast<u32x4_t*>(hb + row * kAtStride + 8 * ch) = L.h[i];
+        const uint32_t wv[4] = {L.w[i].x, L.w[i].y, L.w[i].z, L.w[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wb[(8 * ch + 2 * e) * kBtStride + row] = (uint16_t)(wv[e] & 0xFFFFu);
+            wb[(8 * ch + 2 * e + 1) * kBtStride + row] = (uint16_t)(wv[e] >> 16);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kSkThreads) gate_splitk_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
+                                                               int rows, int D, int r, float* __restrict__ P) {
+    __shared__ __attribute__((aligned(16))) uint16_t hst[2][2][64 * kAtStride];  // [stage][k half][row][k]
+    __shared__ __attribute__((aligned(16))) uint16_t wst[2][2][64 * kBtStride];  // [stage][k half][n][k]
+    __shared__ float red[4][32 * 32];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int sub = wave & 3, kh = wave >> 2, t = threadIdx.x & 255;
+    const int row0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+    const int rs = 32 * (sub & 1), cs = 32 * (sub >> 1);
+    const int kslice = D / kSkSplits, khalf = kslice / 2;
+    const int kbeg = blockIdx.z * kslice + kh * khalf;
+    const int nsteps = khalf / kKStep;
+
+    f32x16_t acc = {};
+    SkLoads cur;
+    sk_load(cur, h, Wg, rows, D, r, row0, n0, kbeg, t);
+    for (int s = 0; s < nsteps; ++s) {
+        uint16_t* hb = hst[s & 1][kh];
+        uint16_t* wb = wst[s & 1][kh];
+        // stage s & 1 was last read at step s - 2, before every wave passed the barrier of step s - 1
+        sk_store(cur, hb, wb, t);
+        if (s + 1 < nsteps) sk_load(cur, h, Wg, rows, D, r, row0, n0, kbeg + (s + 1) * kKStep, t);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(hb + (rs + (lane & 31)) * kAtStride + 16 * kk + 8 * half);
+            const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(wb + (cs + (lane & 31)) * kBtStride + 16 * kk + 8 * half);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+        }
+    }
+    if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[sub][i * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (kh == 0) {
+        float* out = P + (size_t)blockIdx.z * rows * r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = row0 + rs + 8 * (i >> 2) + 4 * half + (i & 3);
+            const int n = n0 + cs + (lane & 31);
+            if (m < rows) out[(size_t)m * r + n] = acc[i] + red[sub][i * 64 + lane];
+        }
+    }
+}
+
+// H = sigmoid(((p0 + p1) + p2) + p3), four values per thread (rows * r is a multiple of 64)
+__global__ void __launch_bounds__(256) gate_reduce_kernel(const float* __restrict__ P, size_t n, float* __restrict__ H) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x * 4;
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+        f32x4_t z = *reinterpret_cast<const f32x4_t*>(P + i);
+#pragma unroll
+        for (int sl = 1; sl < kSkSplits; ++sl) {
+            const f32x4_t p = *reinterpret_cast<const f32x4_t*>(P + sl * n + i);
+            z.x += p.x;
+            z.y += p.y;
+            z.z += p.z;
+            z.w += p.w;
+        }
+        *reinterpret_cast<f32x4_t*>(H + i) = f32x4_t{1.0f / (1.0f + __expf(-z.x)), 1.0f / (1.0f + __expf(-z.y)),
+                                                     1.0f / (1.0f + __expf(-z.z)), 1.0f / (1.0f + __expf(-z.w))};
+    }
+}
+
 }  // namespace
 
-hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, hipStream_t st) {
+size_t gate_splitk_bytes(int rows, int D, int r) {
+    if (rows <= 0 || r % 64 != 0 || D % (kSkSplits * 2 * kKStep) != 0) return 0;
+    return (size_t)kSkSplits * (size_t)rows * (size_t)r * sizeof(float);
+}
+
+hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, void* workspace,
+                       size_t workspace_bytes, hipStream_t st) {
+    const size_t need = gate_splitk_bytes(rows, D, r);
+    if (need > 0 && workspace && workspace_bytes >= need && ((uintptr_t)workspace & 15u) == 0 && ((uintptr_t)H & 15u) == 0) {
+        float* P = static_cast<float*>(workspace);
+        hipLaunchKernelGGL(gate_splitk_kernel, dim3((rows + 63) / 64, r / 64, kSkSplits), dim3(kSkThreads), 0, st, h, Wg,
+                           rows, D, r, P);
+        const size_t n = (size_t)rows * r;
+        const size_t blocks = std::min<size_t>((n / 4 + 255) / 256, 4096);
+        hipLaunchKernelGGL(gate_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, P, n, H);
+        return hipGetLastError();
+    }
     const dim3 grid((rows + 31) / 32, r / 32), block(kGateThreads);
     hipLaunchKernelGGL(gate_kernel, grid, block, 0, st, h, Wg, rows, D, r, H);
     return hipGetLastError();

@@ -173,7 +173,12 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st
 hipError_t launch_stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, hipStream_t st);
 
 // gate: H = sigmoid(h Wg)
-hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, hipStream_t st);
+// Workspace bytes of the split-K gate for these sizes (0: the single-kernel form serves them).
+size_t gate_splitk_bytes(int rows, int D, int r);
+// The split-K form when a large enough 16-byte aligned workspace is given (and H is 16-byte aligned), else the
+// single kernel.
+hipError_t launch_gate(const uint16_t* h, const uint16_t* Wg, int rows, int D, int r, float* H, void* workspace,
+                       size_t workspace_bytes, hipStream_t st);
 
 // selector
 size_t topk_workspace_bytes(int rows, int V, int topk);

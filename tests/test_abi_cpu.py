@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     import rank_markov_draft_amd as D
-    assert D.dspark_abi_version() == 1
+    assert D.dspark_abi_version() == 2
     assert lib.dspark_status_str(0) == b"DSPARK_OK"
     assert lib.dspark_status_str(3) == b"DSPARK_EWORKSPACE"
     assert lib.dspark_status_str(99) == b"DSPARK_UNKNOWN_STATUS"
@@ -122,9 +122,12 @@ def test_selector_gate_topk_argument_errors(lib):
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 8192, 16, 1025, 0, 0, 1.0, FAKE, None, None, None, FAKE, 1 << 20, None) == 2
     assert s(FAKE, FAKE, FAKE, 1, FAKE, None, 2, 2, 100, 16, 16, 0, 0, 1.0, FAKE, None, None, None, FAKE, 8, None) == 3
     g = lib.dspark_gate
-    assert g(None, FAKE, 4, 256, 32, FAKE, None) == 1
-    assert g(FAKE, FAKE, 4, 100, 32, FAKE, None) == 2
-    assert g(FAKE, FAKE, 4, 256, 20, FAKE, None) == 2
+    assert g(None, FAKE, 4, 256, 32, FAKE, None, 0, None) == 1
+    assert g(FAKE, FAKE, 4, 100, 32, FAKE, None, 0, None) == 2
+    assert g(FAKE, FAKE, 4, 256, 20, FAKE, None, 0, None) == 2
+    need = lib.dspark_gate_workspace_bytes(1024, 4096, 256)
+    assert g(FAKE, FAKE, 1024, 4096, 256, FAKE, FAKE, need - 16, None) == 1 and "workspace" in _err(lib)
+    assert g(FAKE, FAKE, 1024, 4096, 256, FAKE, ctypes.c_void_p(0x1008), need, None) == 1 and "aligned" in _err(lib)
     t = lib.dspark_topk
     assert t(FAKE, 100, 4, 100, 0, FAKE, None, None, 0, None) == 1
     assert t(FAKE, 50, 4, 100, 4, FAKE, None, None, 0, None) == 1
@@ -132,6 +135,17 @@ def test_selector_gate_topk_argument_errors(lib):
     p = lib.dspark_pack_w2
     assert p(None, 10, 10, 1, FAKE, None) == 1
     assert p(FAKE, 10, 10, 9, FAKE, None) == 1
+
+
+def test_gate_workspace_bytes(lib):
+    """The split-k gate takes 4 fp32 partial sums per output; sizes it does not take ask for none."""
+    w = lib.dspark_gate_workspace_bytes
+    assert w(1024, 4096, 256) == 4 * 1024 * 256 * 4
+    assert w(100, 1024, 256) == 4 * 100 * 256 * 4
+    assert w(64, 512, 64) == 4 * 64 * 64 * 4
+    assert w(5, 256, 32) == 0        # r not a multiple of 64
+    assert w(64, 256, 64) == 0       # D not a multiple of 512
+    assert w(0, 4096, 256) == 0 and w(4, 100, 32) == 0
 
 
 def test_stream_read_argument_errors(lib):

@@ -176,16 +176,34 @@ def test_gated_selector_with_unit_gate_is_the_markov_head_on_the_candidates(D, m
 
 # -------------------------------------------------------------------------------------------- gate
 
-@pytest.mark.parametrize("rows,Dm,r", [(5, 256, 32), (64, 512, 64), (100, 1024, 256)])
-def test_gate_parity(D, rows, Dm, r):
+@pytest.mark.parametrize("split_k", [True, False], ids=["split-k", "single"])
+@pytest.mark.parametrize("rows,Dm,r", [(5, 256, 32), (64, 512, 64), (100, 1024, 256), (130, 4096, 128)])
+def test_gate_parity(D, rows, Dm, r, split_k):
+    """Both forms against the oracle (the split-k form takes r % 64 == 0 and D % 512 == 0; rows 100 and 130
+    leave a ragged 64-row tile)."""
     rng = np.random.default_rng(rows)
     h = S.f32_to_bf16(rng.standard_normal((rows, Dm)).astype(np.float32))
     Wg = S.f32_to_bf16((rng.standard_normal((Dm, r)) * 0.05).astype(np.float32))
-    H = host(D.dspark_gate(t_w(h), t_w(Wg)))
+    H = host(D.dspark_gate(t_w(h), t_w(Wg), split_k=split_k))
     ref = O.gate(h, Wg)
     assert np.abs(H - ref).max() <= 1e-3
-    H0 = host(D.dspark_gate(t_w(h), t_w(np.zeros_like(Wg))))
+    H0 = host(D.dspark_gate(t_w(h), t_w(np.zeros_like(Wg)), split_k=split_k))
     assert np.all(H0 == 0.5)
+
+
+def test_gate_forms_agree_at_full_size(D):
+    """rows = 1024 (B = 64, K = 16), D = 4096, r = 256: the split-k and single-launch forms differ only in
+    the order of the fp32 sums; twice through one workspace gives the same bits."""
+    w = S.workload("gated")
+    h, Wg = t_w(w.h), t_w(w.Wg)
+    rows = h.numel() // Wg.shape[0]
+    ws = torch.empty(D.dspark_gate_workspace_bytes(rows, Wg.shape[0], Wg.shape[1]), dtype=torch.uint8, device=h.device)
+    assert ws.numel() == 4 * rows * Wg.shape[1] * 4
+    a = host(D.dspark_gate(h, Wg, workspace=ws))
+    b = host(D.dspark_gate(h, Wg, workspace=ws))
+    c = host(D.dspark_gate(h, Wg, split_k=False))
+    assert np.array_equal(a, b)
+    assert np.abs(a - c).max() <= 1e-6
 
 
 def test_full_gated_workload(D):
