@@ -197,13 +197,41 @@ def test_gate_forms_agree_at_full_size(D):
     w = S.workload("gated")
     h, Wg = t_w(w.h), t_w(w.Wg)
     rows = h.numel() // Wg.shape[0]
-    ws = torch.empty(D.dspark_gate_workspace_bytes(rows, Wg.shape[0], Wg.shape[1]), dtype=torch.uint8, device=h.device)
+    ws = torch.full((D.dspark_gate_workspace_bytes(rows, Wg.shape[0], Wg.shape[1]),), 0xA5, dtype=torch.uint8,
+                    device=h.device)  # arbitrary contents: the partial sums are written before they are read
     assert ws.numel() == 4 * rows * Wg.shape[1] * 4
     a = host(D.dspark_gate(h, Wg, workspace=ws))
     b = host(D.dspark_gate(h, Wg, workspace=ws))
     c = host(D.dspark_gate(h, Wg, split_k=False))
     assert np.array_equal(a, b)
     assert np.abs(a - c).max() <= 1e-6
+
+
+def test_gate_graph_replays(D):
+    """The split-k gate (its two launches) captured in a HIP graph: every replay, with eager calls between,
+    equals the eager call."""
+    rng = np.random.default_rng(7)
+    rows, Dm, r = 192, 1024, 128
+    h = t_w(S.f32_to_bf16(rng.standard_normal((rows, Dm)).astype(np.float32)))
+    Wg = t_w(S.f32_to_bf16((rng.standard_normal((Dm, r)) * 0.05).astype(np.float32)))
+    ws = torch.empty(D.dspark_gate_workspace_bytes(rows, Dm, r), dtype=torch.uint8, device=h.device)
+    out = torch.empty((rows, r), dtype=torch.float32, device=h.device)
+    eager = host(D.dspark_gate(h, Wg, workspace=ws))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        D.dspark_gate(h, Wg, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        D.dspark_gate(h, Wg, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), eager), i
+        assert np.array_equal(host(D.dspark_gate(h, Wg, workspace=ws)), eager), i
 
 
 def test_full_gated_workload(D):
