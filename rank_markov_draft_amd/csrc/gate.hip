@@ -132,7 +132,8 @@ __global__ void __launch_bounds__(kGateThreads) gate_kernel(const uint16_t* __re
 // split (12.9 + 4.0 us of kernel time).  Not kept: two k steps of loads in flight (19.2 us); the slices summed
 // by the last of a tile's workgroups to finish (per-tile arrival words) instead of a second launch: 23.2 us
 // with the partial sums stored and read at device scope, 62.8 us with a device-wide fence per workgroup
-// instead (each wrote back its XCD's L2).
+// instead (each wrote back its XCD's L2); the sum as one workgroup per 64 x 64 tile on the split-K grid, so that
+// it runs on the XCD that wrote the tile (20.2 against 19.0 us: 64 workgroups are too few).
 constexpr int kSkSplits = 4;
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = 64 * kSkWaves;
