@@ -207,6 +207,24 @@ def test_gate_forms_agree_at_full_size(D):
     assert np.abs(a - c).max() <= 1e-6
 
 
+def test_gate_misaligned_output_takes_the_unsplit_form(D):
+    """A workspace with an H that is not 16-byte aligned: the call falls back to the unsplit form (bit for bit
+    the split_k=False result) instead of the split-k sum's 16-byte stores."""
+    rng = np.random.default_rng(11)
+    rows, Dm, r = 128, 1024, 128
+    hn = S.f32_to_bf16(rng.standard_normal((rows, Dm)).astype(np.float32))
+    Wn = S.f32_to_bf16((rng.standard_normal((Dm, r)) * 0.05).astype(np.float32))
+    h, Wg = t_w(hn), t_w(Wn)
+    flat = torch.empty(rows * r + 1, dtype=torch.float32, device=h.device)
+    out = flat[1:].view(rows, r)
+    assert out.data_ptr() % 16 != 0
+    ws = torch.empty(D.dspark_gate_workspace_bytes(rows, Dm, r), dtype=torch.uint8, device=h.device)
+    D.dspark_gate(h, Wg, out=out, workspace=ws)
+    ref = host(D.dspark_gate(h, Wg, split_k=False))
+    assert np.array_equal(host(out), ref)
+    assert np.abs(ref - O.gate(hn, Wn)).max() <= 1e-3
+
+
 def test_gate_graph_replays(D):
     """The split-k gate (its two launches) captured in a HIP graph: every replay, with eager calls between,
     equals the eager call."""
