@@ -40,8 +40,11 @@ def test_topk_exact(D, V, k):
     assert np.array_equal(host(val), rval)
 
 
-@pytest.mark.parametrize("V,k", [(64, 64), (512, 512), (300, 40), (4096, 100)])
+@pytest.mark.parametrize("V,k", [(64, 64), (512, 512), (300, 40), (4096, 100), (65, 65), (100, 77), (2000, 1999),
+                                 (4096, 4096)])
 def test_topk_large_k_small_vocab(D, V, k):
+    """k > 64 at V <= 4096 takes the whole-row bitonic sort in LDS (padded to a power of two: 65 -> 128,
+    100 -> 128, 2000 -> 2048; 4096 fills it)."""
     U = _tie_rows(12, V, seed=k)
     idx, val = D.dspark_topk(t_f32(U), k)
     ridx, rval = O.topk(U, k)
