@@ -21,7 +21,8 @@
 // leaving the transpose stores out altogether would save 2.5 us); each workgroup taking its k chunks in a
 // rotated order so that the workgroups sharing h rows or Wg columns do not read the same lines at once
 // (20.7 us).  What remains is the tiling: the 32 x 32 tiles re-read h once per column block and Wg once per
-// row block, about 128 MB of L2 reads for 10.5 MB of operands.
+// row block, about 128 MB of L2 reads for 10.5 MB of operands; the split-K form below (taken when the caller
+// gives a workspace) uses 64 x 64 tiles and halves that.
 #include <algorithm>
 
 #include "internal.hpp"
